@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module holds no attention arithmetic: it only draws Gaussian tensors, rounds
+them to the storage dtype and samples row indices.  Both the HIP path and the
+oracle consume its output; neither is imported here.
+
+Workloads (Gaussian Q/K/V, as in the verification block of "Breaking the Memory
+Wall: A Deep Dive into FlashAttention" -- "Implementation: Simulating
+FlashAttention in PyTorch", which draws q, k, v with randn):
+
+  name                              pass  dtype  B  H   N      d    causal  seed
+  fwd_f32_b2h1_n512_d64             fwd   f32    2  1   512    64   no      1
+  fwd_bf16_b8h16_n2048_d64          fwd   bf16   8  16  2048   64   no      2
+  fwd_bf16_causal_b4h32_n8192_d128  fwd   bf16   4  32  8192   128  yes     3  (Q drawn x3)
+  fwd_bf16_causal_b1h32_n16384_d128 fwd   bf16   1  32  16384  128  yes     4  (rows seed 1004)
+  bwd_bf16_causal_b4h16_n4096_d128  bwd   bf16   4  16  4096   128  yes     5
+
+Recipe: ``np.random.default_rng(seed).standard_normal(shape, dtype=float32)`` drawn
+in the order Q, K, V (then dO for backward cases); Q multiplied by ``q_scale`` in
+fp32; then rounded to the storage dtype (bf16 with round-to-nearest-even).  The
+scale passed to attention is 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+CONFIGS = {
+    "fwd_f32_b2h1_n512_d64": dict(pass_="fwd", dtype="f32", B=2, H=1, N=512, d=64,
+                                  causal=False, seed=1, q_scale=1.0),
+    "fwd_bf16_b8h16_n2048_d64": dict(pass_="fwd", dtype="bf16", B=8, H=16, N=2048, d=64,
+                                     causal=False, seed=2, q_scale=1.0),
+    "fwd_bf16_causal_b4h32_n8192_d128": dict(pass_="fwd", dtype="bf16", B=4, H=32, N=8192,
+                                             d=128, causal=True, seed=3, q_scale=3.0),
+    "fwd_bf16_causal_b1h32_n16384_d128": dict(pass_="fwd", dtype="bf16", B=1, H=32, N=16384,
+                                              d=128, causal=True, seed=4, q_scale=1.0,
+                                              row_seed=1004, rows_per_head=256),
+    "bwd_bf16_causal_b4h16_n4096_d128": dict(pass_="bwd", dtype="bf16", B=4, H=16, N=4096,
+                                             d=128, causal=True, seed=5, q_scale=1.0),
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bfloat16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def draw(shape, seed: int, names=("q", "k", "v"), q_scale: float = 1.0) -> dict:
+    """Draw float32 N(0,1) tensors of ``shape`` in the order given (default Q, K, V)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name in names:
+        out[name] = rng.standard_normal(shape, dtype=np.float32)
+    if "q" in out and q_scale != 1.0:
+        out["q"] *= np.float32(q_scale)
+    return out
+
+
+def make_case(B: int, H: int, N: int, d: int, dtype: str, seed: int, q_scale: float = 1.0,
+              with_grad: bool = False) -> dict:
+    """Inputs of one case, as stored values.
+
+    Returns ``{"dtype", "scale", name: {"bits" or None, "values": float32 array}}`` for
+    names q, k, v (and "do" if ``with_grad``).  For bf16, ``values`` holds the exact
+    float32 value of the stored bf16 bits; for f32 it is the drawn array itself.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    names = ("q", "k", "v", "do") if with_grad else ("q", "k", "v")
+    raw = draw((B, H, N, d), seed, names, q_scale)
+    case = {"dtype": dtype, "scale": 1.0 / math.sqrt(d), "shape": (B, H, N, d)}
+    for name, arr in raw.items():
+        if dtype == "bf16":
+            bits = bf16_bits(arr)
+            case[name] = {"bits": bits, "values": bf16_bits_to_f32(bits)}
+        else:
+            case[name] = {"bits": None, "values": arr}
+    return case
+
+
+def make_config(name: str) -> dict:
+    """The case for one named workload in ``CONFIGS``."""
+    c = CONFIGS[name]
+    return make_case(c["B"], c["H"], c["N"], c["d"], c["dtype"], c["seed"], c["q_scale"],
+                     with_grad=(c["pass_"] == "bwd"))
+
+
+def sample_rows(B: int, H: int, N: int, rows_per_head: int, seed: int) -> np.ndarray:
+    """Per (b, h), ``rows_per_head`` distinct query rows drawn uniformly without replacement.
+
+    Returns int64 [B, H, R], each row sorted ascending.
+    """
+    rng = np.random.default_rng(seed)
+    r = min(rows_per_head, N)
+    out = np.empty((B, H, r), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = np.sort(rng.choice(N, size=r, replace=False))
+    return out

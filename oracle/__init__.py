@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for exact attention -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package.  The HIP library and its Python binding never do,
+and this package imports nothing from them.
+
+Every function here is pinned by a ``-m "not gpu"`` test in
+``tests/test_oracle_pins.py`` (closed forms, invariants, brute force on tiny
+inputs, finite differences and a library special case); none is "parity unpinned".
+"""
+from .attention import backward, forward, forward_rows, probabilities, scores  # noqa: F401
+from .online import chunk_merge, tiled_forward  # noqa: F401
