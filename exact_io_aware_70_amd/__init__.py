@@ -1,0 +1,162 @@
+"""Python binding of libfa.so (exact IO-aware attention on MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind
+the C ABI declared in ``include/fa.h``.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing or cannot be loaded, every call raises.
+
+    o, lse = fa_fwd(q, k, v, causal=True)               # q, k, v: [B, H, N, d] on the GPU
+    dq, dk, dv = fa_bwd(q, k, v, o, lse, do, causal=True)
+
+Tensors must be contiguous, on one GPU, all float32 or all bfloat16, d in {64, 128}.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FAError", "library_path", "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_size",
+           "fa_status_string", "fa_version", "FA_OK", "FA_F32", "FA_BF16"]
+
+FA_OK = 0
+FA_F32 = 0
+FA_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FAError(RuntimeError):
+    """A libfa call returned a non-zero fa_status."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {fa_status_string(code)} (status {code})")
+
+
+def library_path() -> str:
+    return os.environ.get("FA_LIBRARY", os.path.join(_HERE, "libfa.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa.so once and declare the C signatures; raises if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfa.so not found at {path}; build it with "
+                           "`python -m exact_io_aware_70_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _LIB = lib
+    return lib
+
+
+def fa_status_string(code: int) -> str:
+    return load_library().fa_status_string(int(code)).decode()
+
+
+def fa_version() -> int:
+    return int(load_library().fa_version())
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int, dtype: int) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d, dtype))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check(name: str, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fa_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None):
+    """Forward pass: returns (o [B,H,N,d] in q's dtype, lse [B,H,N] float32).
+
+    ``o`` and ``lse`` may be passed preallocated; ``scale`` defaults to 1/sqrt(d).
+    Work is enqueued on ``stream`` (default: the current torch stream) without waiting.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check("o", o, (B, H, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, sc, 1 if causal else 0, _dtype_code(q), _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=False,
+           workspace=None, stream=None):
+    """Backward pass: returns (dq, dk, dv) for the loss sum(o * do).
+
+    ``o`` and ``lse`` are what fa_fwd returned for (q, k, v).  ``workspace`` (a uint8 device
+    tensor of at least fa_bwd_workspace_size bytes) may be passed to avoid an allocation.
+    """
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0, code,
+                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                    _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,84 @@
+// C ABI of libfa.so: argument validation, workspace sizing and dispatch to the kernel
+// launchers.  Validation touches no HIP API, so every error path below can be exercised
+// on a machine without a GPU; nothing is enqueued unless all checks pass.
+#include "../../include/fa.h"
+
+#include <stdint.h>
+
+#include <cmath>
+
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by the forward and backward entry points.
+int check_common(int B, int H, int N, int d, float scale, int dtype) {
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    // One workgroup per (batch, head, 64-row tile) at most: keep the 1-D grid in range.
+    const long long tiles = (long long)B * H * ((N + 63) / 64);
+    if (tiles > 0x7fffffffLL) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    const int st = check_common(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype};
+    const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
+    if (check_common(B, H, N, d, 1.0f, dtype) != FA_OK) return 0;
+    // D_i = rowsum(dout * o): one float per (batch, head, row).
+    return round_up((size_t)B * H * N * sizeof(float), 256);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    const int st = check_common(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype) || !aligned(workspace, 256))
+        return FA_ERR_WORKSPACE;
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0, dtype,
+                  static_cast<float*>(workspace)};
+    const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK: success";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H and N must be >= 1 and the grid must fit in 2^31 - 1 tiles";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64 or 128, dtype FA_F32 or FA_BF16, scale finite and > 0";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned (lse 4-byte)";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a kernel launch";
+        default: return "unknown fa_status code";
+    }
+}
+
+int fa_version(void) { return FA_VERSION; }
+
+}  // extern "C"

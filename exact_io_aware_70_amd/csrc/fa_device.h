@@ -1,0 +1,81 @@
+// Device-side building blocks shared by the forward and backward kernels (gfx950 only).
+//
+// MFMA register layouts used throughout (checked on gfx950 by a lane-layout probe):
+//   v_mfma_f32_32x32x16_bf16  A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + i], i = 0..7
+//                             B (16 x 32): lane l holds B[8 * (l / 32) + i][l % 32]
+//                             C (32 x 32): lane l, register r holds
+//                                          C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+//   v_mfma_f32_32x32x2_f32    A: A[l % 32][l / 32], B: B[l / 32][l % 32], C as above.
+// Only the pairing of A's and B's k index matters for a contraction, so any consistent
+// permutation of k between the two operands is allowed; the kernels use that freedom to
+// feed an accumulator straight back in as the next product's operand.
+//
+// ds_read_b64_tr_b16 (gfx950): inside each group of 16 lanes, lane 4e + q supplies the
+// address of four consecutive 16-bit values; lane i of the group receives, as element e,
+// value (i % 4) of lane 4e + i / 4.  Pointing lane 4e + q at row r0 + e, column c0 + 4q of
+// a row-major tile therefore hands lane i the column c0 + i of rows r0..r0+3: a
+// transposed 4 x 16 block in one instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for -infinity as the initial running maximum: exp2 of (it - finite)
+// is exactly 0 and (it - it) is 0, so no inf - inf = NaN can arise.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Four 16-bit values, transposed across each 16-lane group (see the header comment).
+__device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+    i16x8 t = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, t);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Round eight consecutive accumulator values (starting at `first`) to bf16, RNE.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& acc, int first) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)acc[first + i];
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane (l ^ 32): the other half of the wave.
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Map a linear workgroup id to a logical one so that consecutive logical ids land on the
+// same XCD (workgroups are dealt to the 8 XCDs round-robin); keeps one head's tiles
+// inside one L2.
+__device__ __forceinline__ int xcd_remap(int b, int g) {
+    return (g % 8 == 0) ? (b % 8) * (g / 8) + b / 8 : b;
+}
+
+}  // namespace fa

@@ -1,0 +1,48 @@
+// Host-side interface between the C ABI (fa_api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, N, d;
+    float scale;
+    int causal;
+    int dtype;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, H, N, d;
+    float scale;
+    int causal;
+    int dtype;
+    float* delta;  // workspace: D_i = rowsum(dout * o), float [B, H, N]
+};
+
+// Enqueue the forward / backward kernels on `st`; return hipGetLastError() of the launches.
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+
+// Query tiles per (batch, head) of the forward grid.
+long long fwd_grid_tiles(int N, int dtype);
+
+}  // namespace fa

@@ -1,0 +1,105 @@
+/*
+ * fa.h -- exact IO-aware self-attention for AMD MI355X (gfx950): the C ABI of libfa.so.
+ *
+ * Computes O = softmax(scale * Q K^T) V per (batch, head) without ever writing the
+ * N x N score or probability matrix to HBM: the forward pass walks key/value tiles
+ * with an online (running max, running sum) softmax and keeps only the per-row
+ * logsumexp; the backward pass recomputes each score tile from Q, K and that
+ * logsumexp instead of reading a stored probability matrix.
+ *
+ * Sources (page title -- section):
+ *   "Breaking the Memory Wall: A Deep Dive into FlashAttention" -- "The Problem: The
+ *     Memory Wall" (P = softmax(Q K^T / sqrt(d))), "The Solution: IO-Awareness &
+ *     Tiling" items 1-3 (tiling, incremental softmax, backward recomputation from the
+ *     saved normalisation factors);
+ *   "How does FlashAttention optimize memory and speed via tiling?" -- "Core Technical
+ *     Innovations in FlashAttention" (the running max / running sum merge);
+ *   "How FlashAttention Actually Works" -- "The Backward Pass: Recomputation".
+ *
+ * Conventions shared by every entry point
+ *   - Tensors q, k, v, o, dout, dq, dk, dv are DEVICE pointers to contiguous
+ *     [B, H, N, d] arrays, d fastest, all of element type `dtype`
+ *     (FA_F32: IEEE float; FA_BF16: bfloat16 stored as 16-bit words).
+ *   - lse is a DEVICE pointer to float [B, H, N]: the natural-log logsumexp of row i
+ *     of scale * Q K^T (over its visible keys).
+ *   - scale multiplies the logits and is used as given (callers pass 1/sqrt(d)).
+ *   - causal != 0 masks key j > query i (square, diagonal visible).
+ *   - stream is a hipStream_t (NULL = the default stream).  All work is enqueued on
+ *     it in order; no call waits for the GPU, allocates or frees memory, or keeps
+ *     state between calls.  The caller owns every buffer.
+ *   - Arithmetic: bf16 inputs are multiplied on bf16 MFMA with fp32 accumulation;
+ *     probabilities and dS are rounded to bf16 before their products; outputs are
+ *     rounded to the input dtype (round to nearest even).  The fp32 path uses fp32
+ *     MFMA throughout.
+ *   - Supported: B, H, N >= 1; d in {64, 128}; B*H*ceil(N/64) < 2^31.
+ *   - Errors: arguments are validated before anything is enqueued; on failure a
+ *     negative fa_status is returned and nothing runs.  A failed kernel launch returns
+ *     FA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any HIP work.
+ *   - Aliasing: outputs must not overlap inputs or each other (not checked).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,       /* B, H or N < 1, or the grid would exceed 2^31 - 1 tiles */
+    FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128} or unknown dtype */
+    FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
+    FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float).
+ * "Breaking the Memory Wall" -- "The Solution: IO-Awareness & Tiling", items 1-2:
+ * K/V tiles are streamed past each query tile, the running max m and running sum l
+ * are merged per tile, the unnormalised output is rescaled by e^{m_old - m_new},
+ * and O = acc / l, lse = m + ln l at the end.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (>= 256; 0 if the sizes are
+ * invalid).  Only the size matters; the contents need no initialisation.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass for the loss L = sum(O * dout): writes dq, dk, dv [B,H,N,d] (dtype).
+ * q, k, v are the forward inputs; o and lse are what fa_fwd wrote for them; dout is
+ * dL/dO.  Score tiles are recomputed from q, k and lse ("How FlashAttention Actually
+ * Works" -- "The Backward Pass: Recomputation"; "Breaking the Memory Wall" -- item 3).
+ * With P = exp(scale q k^T - lse), dP = dout v^T, D_i = rowsum(dout * o)_i and
+ * dS = P * (dP - D):  dv = P^T dout,  dq = scale dS k,  dk = scale dS^T q.
+ * workspace: device memory of at least fa_bwd_workspace_size() bytes, 256-byte aligned,
+ * owned by the caller, not shared with a concurrent call.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static, never-NULL description of a status code (unknown codes included). */
+const char* fa_status_string(int status);
+
+/* FA_VERSION of the built library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,138 @@
+"""The C ABI boundary on the CPU: libfa.so loads, exports what include/fa.h declares, and
+rejects bad arguments with the documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import exact_io_aware_70_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+                                reason="libfa.so not built (python -m exact_io_aware_70_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_is_plain_c():
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    res = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = fa.load_library()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings():
+    assert fa.fa_version() == 100
+    seen = set()
+    for code in [0, -1, -2, -3, -4, -5, -6]:
+        s = fa.fa_status_string(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert fa.fa_status_string(12345) == "unknown fa_status code"
+
+
+GOOD = dict(B=2, H=3, N=100, d=64, scale=0.125, causal=0, dtype=1)
+P = 4096  # a fake, 16-byte aligned, never dereferenced address
+
+
+def call_fwd(q=P, k=P, v=P, o=P, lse=P, **kw):
+    a = dict(GOOD, **kw)
+    return fa.load_library().fa_fwd(q, k, v, o, lse, a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                    a["causal"], a["dtype"], None)
+
+
+def call_bwd(ptrs=None, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(GOOD, **kw)
+    p = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P)
+    p.update(ptrs or {})
+    return fa.load_library().fa_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"], p["dv"],
+                                    a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                    ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fwd_null(which):
+    assert call_fwd(**{which: None}) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(H=0), -2), (dict(N=0), -2), (dict(N=-5), -2),
+    (dict(d=32), -3), (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(scale=0.0), -3), (dict(scale=-0.1), -3), (dict(scale=float("inf")), -3), (dict(scale=float("nan")), -3),
+    (dict(B=1 << 20, H=1 << 12, N=1 << 12), -2),
+])
+def test_fwd_bad_sizes(kw, code):
+    assert call_fwd(**kw) == code
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_fwd_misaligned(which):
+    assert call_fwd(**{which: P + 8}) == -4
+    assert call_fwd(lse=P + 2) == -4
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"])
+def test_bwd_null(which):
+    assert call_bwd(ptrs={which: None}) == -1
+
+
+def test_bwd_workspace():
+    need = fa.fa_bwd_workspace_size(2, 3, 100, 64, 1)
+    assert need >= 2 * 3 * 100 * 4 and need % 256 == 0
+    assert call_bwd(ws=None) == -5
+    assert call_bwd(ws_bytes=need - 1) == -5
+    assert call_bwd(ws=P + 16) == -5  # not 256-byte aligned
+    assert fa.fa_bwd_workspace_size(0, 3, 100, 64, 1) == 0
+    assert fa.fa_bwd_workspace_size(2, 3, 100, 48, 1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [(dict(N=0), -2), (dict(d=80), -3), (dict(dtype=5), -3), (dict(scale=0.0), -3)])
+def test_bwd_bad_sizes(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_misaligned():
+    for which in ["q", "k", "v", "o", "do", "dq", "dk", "dv"]:
+        assert call_bwd(ptrs={which: P + 4}) == -4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No CPU fallback: a missing library is an error, not a silent alternative path."""
+    monkeypatch.setenv("FA_LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fa, "_LIB", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        fa.load_library()
+
+
+def test_product_does_not_import_oracle():
+    """The package and its sources never reference the oracle."""
+    pkg = os.path.join(ROOT, "exact_io_aware_70_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f

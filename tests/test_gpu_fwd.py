@@ -1,0 +1,136 @@
+"""GPU parity of fa_fwd against the fp64 oracle (element by element), through the C ABI.
+
+Small cases span several query and key tiles with ragged tails and are compared in full;
+the named workloads run at their full sizes in the launch configuration the bench times,
+compared in full (small ones) or on seeded row samples the oracle computes one by one."""
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+from tests.gpu_util import assert_parity, gpu_available, log, to_device, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def run_fwd(case, causal):
+    import exact_io_aware_70_amd as fa
+    q, k, v = (to_device(case, n) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, scale=case["scale"], causal=causal)
+    import torch
+    torch.cuda.synchronize()
+    return q, k, v, o, lse
+
+
+def check_full(case, causal, label):
+    log(f"[fwd] {label}")
+    _, _, _, o, lse = run_fwd(case, causal)
+    ref_o, ref_lse = oracle.forward(case["q"]["values"], case["k"]["values"], case["v"]["values"],
+                                    case["scale"], causal)
+    assert_parity("O", to_f64(o), ref_o, case["dtype"])
+    assert_parity("lse", to_f64(lse), ref_lse, case["dtype"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 300, 1000])
+def test_fwd_small(dtype, d, causal, N):
+    case = fa_inputs.make_case(2, 2, N, d, dtype, seed=100 + N + d)
+    check_full(case, causal, f"small {dtype} d={d} causal={causal} N={N}")
+
+
+def test_fwd_large_logits_bf16():
+    """Q drawn x3 (logits std ~3) with a long causal row: the online rescale is exercised."""
+    case = fa_inputs.make_case(1, 4, 2000, 128, "bf16", seed=77, q_scale=3.0)
+    check_full(case, True, "bf16 causal q x3 N=2000")
+
+
+def test_fwd_config_f32_b2h1_n512_d64():
+    case = fa_inputs.make_config("fwd_f32_b2h1_n512_d64")
+    check_full(case, False, "fwd_f32_b2h1_n512_d64 (all outputs)")
+
+
+def test_fwd_config_bf16_b8h16_n2048_d64():
+    case = fa_inputs.make_config("fwd_bf16_b8h16_n2048_d64")
+    check_full(case, False, "fwd_bf16_b8h16_n2048_d64 (all outputs)")
+
+
+def _check_rows(name, rows):
+    cfg = fa_inputs.CONFIGS[name]
+    case = fa_inputs.make_config(name)
+    log(f"[fwd] {name} (sampled rows: {rows.shape[-1]} per head)")
+    _, _, _, o, lse = run_fwd(case, cfg["causal"])
+    import torch
+    idx = torch.from_numpy(rows).to("cuda")
+    o_rows = torch.gather(o, 2, idx[..., None].expand(-1, -1, -1, o.shape[-1]))
+    lse_rows = torch.gather(lse, 2, idx)
+    ref_o, ref_lse = oracle.forward_rows(case["q"]["values"], case["k"]["values"], case["v"]["values"],
+                                         case["scale"], cfg["causal"], rows)
+    assert_parity("O rows", to_f64(o_rows), ref_o, case["dtype"])
+    assert_parity("lse rows", to_f64(lse_rows), ref_lse, case["dtype"])
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def _rows_with_edges(B, H, N, per_head, seed):
+    rows = fa_inputs.sample_rows(B, H, N, per_head, seed)
+    edges = np.array([0, 1, 63, 64, 127, 128, 255, 256, N // 2, N - 2, N - 1])
+    return np.concatenate([rows, np.broadcast_to(edges, (B, H, len(edges)))], axis=2)
+
+
+def test_fwd_config_bf16_causal_b4h32_n8192_d128():
+    """Q x3 stress config: every head, 64 random rows plus tile-edge rows each."""
+    cfg = fa_inputs.CONFIGS["fwd_bf16_causal_b4h32_n8192_d128"]
+    _check_rows("fwd_bf16_causal_b4h32_n8192_d128", _rows_with_edges(cfg["B"], cfg["H"], cfg["N"], 64, 1003))
+
+
+def test_fwd_config_bf16_causal_b1h32_n16384_d128():
+    """Long context: the seeded 256 rows per head (plus row 0 and row N-1)."""
+    cfg = fa_inputs.CONFIGS["fwd_bf16_causal_b1h32_n16384_d128"]
+    rows = fa_inputs.sample_rows(cfg["B"], cfg["H"], cfg["N"], cfg["rows_per_head"], cfg["row_seed"])
+    rows = np.concatenate([rows, np.broadcast_to(np.array([0, cfg["N"] - 1]), (cfg["B"], cfg["H"], 2))], axis=2)
+    _check_rows("fwd_bf16_causal_b1h32_n16384_d128", rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fwd_deterministic(dtype):
+    """No atomics in the forward: two runs are bitwise identical."""
+    import torch
+    case = fa_inputs.make_case(2, 4, 777, 128, dtype, seed=5)
+    _, _, _, o1, l1 = run_fwd(case, True)
+    _, _, _, o2, l2 = run_fwd(case, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_allocates_nothing():
+    """With outputs preallocated, fa_fwd leaves torch's allocator untouched: no N x N buffer."""
+    import torch
+    import exact_io_aware_70_amd as fa
+    case = fa_inputs.make_case(1, 2, 4096, 128, "bf16", seed=9)
+    q, k, v = (to_device(case, n) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    fa.fa_fwd(q, k, v, o, lse, causal=True)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    assert torch.cuda.max_memory_allocated() == before
+
+
+def test_fwd_closed_forms_on_gpu():
+    """Q = 0: O is the (prefix) mean of V and lse = ln(#visible keys), on the GPU path."""
+    import torch
+    import exact_io_aware_70_amd as fa
+    N, d = 333, 64
+    v = torch.randn(1, 2, N, d, device="cuda", dtype=torch.float32)
+    q = torch.zeros_like(v)
+    k = torch.randn_like(v)
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    prefix = torch.cumsum(v.double(), dim=2) / torch.arange(1, N + 1, device="cuda", dtype=torch.float64)[:, None]
+    assert (o.double() - prefix).abs().max().item() < 1e-5
+    assert (lse.double() - torch.log(torch.arange(1, N + 1, device="cuda", dtype=torch.float64))).abs().max().item() < 1e-5
+    o, lse = fa.fa_fwd(q, k, v, causal=False)
+    assert (o.double() - v.double().mean(dim=2, keepdim=True)).abs().max().item() < 1e-5
