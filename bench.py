@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="fwd_bf16_causal_b4h32_n8192_d128")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=2, help="heads of the workload the CPU oracle runs")
+    p.add_argument("--cpu-heads", type=int, default=16, help="heads of the workload the CPU oracle runs")
     return p.parse_args()
 
 
@@ -74,7 +74,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
-              "(heads shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+              "(heads shard across GPUs with no exchange, so one GPU runs one share).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
