@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--workload", default="fwd_bf16_causal_b4h32_n8192_d128")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=16, help="heads of the workload the CPU oracle runs")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="before the steps, copy this many MiB once with a plain device copy: the reference "
+                        "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM byte counts")
     return p.parse_args()
 
 
@@ -111,6 +114,15 @@ def main():
         fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=sc, causal=causal, workspace=ws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

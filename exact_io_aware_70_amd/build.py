@@ -25,7 +25,8 @@ ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
                 "-Wall", "-Wno-unused-function"]
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
+                "-fno-honor-nans"]
 
 
 def hipcc() -> str:

@@ -71,6 +71,64 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Value held by lane (l ^ 32): the other half of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// Buffer resource (raw, stride 0) over `bytes` bytes starting at `base`, as four SGPRs.
+// Loads through it return 0 for any byte offset at or past `bytes`, so ragged tails need no
+// address clamping.  `base` and `bytes` must be uniform across the wave.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;  // raw buffer, 32-bit data format
+    return r;
+}
+
+// LDS byte address of a __shared__ location (wave-uniform for the stage bases used here).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p);
+}
+
+// 16 bytes per lane from rsrc + voffset straight into LDS: lane l's data lands at byte
+// lds_base + 16 l (M0 holds the wave-uniform base; 64 lanes fill 1 KiB).  Issued as inline
+// assembly so the compiler does not add its own conservative wait before every LDS read;
+// callers order these loads explicitly with wait_vmcnt() and a workgroup barrier.
+__device__ __forceinline__ void load_lds_b128(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(lds_base) : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 encoding: vmcnt[3:0] and vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt left at their maxima.
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Scheduling hints: within the current basic block, ask the scheduler for N repetitions of
+// {DS reads, one MFMA, VALU ops} so the matrix core and the vector ALU work side by side.
+enum : int { kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100 };
+template <int N, int DS, int VALU>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (DS > 0) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, DS, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        if (VALU > 0) __builtin_amdgcn_sched_group_barrier(kSchedVALU, VALU, 0);
+    }
+}
+
+// An empty volatile asm that claims to rewrite the operands: everything computing them must
+// happen before this point, and nothing is emitted.
+template <int A, int B>
+__device__ __forceinline__ void pin_regs(bf16x8 (&v)[A][B]) {
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int b = 0; b < B; ++b) asm volatile("" : "+v"(v[a][b]));
+}
+
 // Map a linear workgroup id to a logical one so that consecutive logical ids land on the
 // same XCD (workgroups are dealt to the 8 XCDs round-robin); keeps one head's tiles
 // inside one L2.

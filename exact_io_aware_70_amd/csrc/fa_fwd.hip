@@ -14,6 +14,8 @@
 // S^T = K Q^T, so a lane holds 32 scores of ONE query row: the row maximum and row sum
 // are in-lane except for one exchange between the two wave halves, and the accumulator
 // of S^T is directly the B operand of O^T += V^T P^T.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -27,25 +29,68 @@ namespace {
 constexpr float kRescaleSlack = 8.0f;
 
 // ------------------------------------------------------------------ bf16, MFMA 32x32x16
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
+// Workgroup: NW waves, each owning QB blocks of 32 query rows (every K/V operand read from
+// LDS feeds QB MFMAs).  K/V stream in sub-tiles of 32 keys through an NS-stage
+// LDS ring filled by buffer loads that write LDS directly (no register staging).  Rows of
+// a stage are stored with their 16-byte chunks XOR-swizzled by (row % 8), which keeps both
+// the row-wise K reads and the transposed V reads free of bank conflicts.
+//
+// Software pipeline per sub-tile i (one barrier each):
+//   exponentials of S(i) on the VALU  ||  S(i+1) = K(i+1) Q^T on the MFMA
+//   O^T += V(i)^T P(i)^T on the MFMA   ||  row sums of P(i), row max of S(i+1)
+template <int D>
+struct FwdTile {
+    static constexpr int BK = 32;          // keys per sub-tile
+    static constexpr int NS = 4;           // LDS stages
+    static constexpr int CPR = D / 8;      // 16-byte chunks per row
+    static constexpr int STAGE = BK * D;   // bf16 elements per tensor per stage
+};
+
+// LDS swizzle: row r of a stage stores its logical 16-byte chunk c at slot c ^ swz_row(r).
+// gfx950's LDS serves 256 bytes per clock to 128-bit reads (64 banks) and 128 bytes per
+// clock to the transposed 64-bit reads.  The K reads of the S^T product fetch one chunk
+// from 16 consecutive rows per 16 lanes, so the 16 rows must land in 16 different 16-byte
+// bank groups; the transposed V reads fetch two chunks from each of 4 consecutive rows per
+// 16 lanes, and run at full rate when those 8 pieces fill one aligned 128-byte span.
+//   D = 128 (256-byte rows): f(r) = (2r mod 8) | (r/4 mod 2) | (r mod 16 >= 8 ? 8 : 0)
+//   D = 64 (128-byte rows, two per 256 bytes): the same idea on row pairs.
+template <int D>
+__device__ __forceinline__ int swz_row(int r) {
+    if constexpr (D == 128) return ((2 * r) & 7) | ((r >> 2) & 1) | (r & 8);
+    const int x = (r >> 1) & 7;
+    return 2 * (x & 3) + ((x >> 2) & 1);
+}
+
+// Element index of (row, col) inside a swizzled stage (col a multiple of 4).
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * D + (((col >> 3) ^ swz_row<D>(row)) << 3) + (col & 7);
+}
+
+// Two waves per SIMD: the register budget stays within 256 VGPRs, so every MFMA keeps its
+// accumulator in ordinary VGPRs and the softmax reads the scores in place.
+template <int D, int NW, int QB, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2) {
-    constexpr int BM = 32 * NW;         // query rows per workgroup
-    constexpr int BN = 64;              // keys per K/V tile
+    using T = FwdTile<D>;
+    constexpr int BK = T::BK, NS = T::NS, CPR = T::CPR, STAGE = T::STAGE;
+    constexpr int RW = 32 * QB;         // query rows per wave
+    constexpr int BM = RW * NW;         // query rows per workgroup
     constexpr int NT = NW * 64;         // threads
-    constexpr int KST = D + 8;          // K row stride in LDS (16-byte pad: conflict-free b128 reads)
-    constexpr int VST = D + 16;         // V row stride in LDS (32-byte pad for transposed reads)
     constexpr int DC = D / 16;          // k-steps of the S^T product
     constexpr int DB = D / 32;          // 32-row blocks of O^T
-    constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int NCH = BN * CPR / NT;  // chunks per thread per tensor per tile
-    static_assert(NCH >= 1 && BN * CPR % NT == 0, "tile / thread mismatch");
+    constexpr int LPT = BK * CPR / NT;  // LDS-direct loads per thread per tensor per sub-tile
+    constexpr int LPS = 2 * LPT;        // ... for K and V together
+    static_assert(LPT >= 1 && BK * CPR % NT == 0, "tile / thread mismatch");
+    static_assert(NS >= 3 && (NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KST];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VST];
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs[NS][STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform across the wave; readfirstlane lets the compiler see that, so
+    // every per-wave decision below is a scalar branch rather than an exec-masked one.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -53,153 +98,246 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
     const int qt = nqt - 1 - (L % nqt);  // heaviest (causal) tiles first
     const int q0 = qt * BM;
     const size_t base = (size_t)bh * N * D;
-    const __bf16* Qh = Q + base;
-    const __bf16* Kh = K + base;
-    const __bf16* Vh = V + base;
+    const int wq0 = q0 + wave * RW;      // first query row of this wave
 
-    const int wq0 = q0 + wave * 32;  // first query row of this wave
-    const int myq = wq0 + l32;       // this lane's query row
-
-    // Q^T fragment as the B operand of S^T = K Q^T, resident for the whole loop.
-    bf16x8 qf[DC];
+    // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop.  Rows past N
+    // read row N - 1: finite values whose results are never stored.
+    bf16x8 qf[QB][DC];
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) {
-        if (myq < N) qf[kc] = load_bf16x8(Qh + (size_t)myq * D + 16 * kc + 8 * half);
-        else qf[kc] = bf16x8{};
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = min(wq0 + 32 * qb + l32, N - 1);
+#pragma unroll
+        for (int kc = 0; kc < DC; ++kc) qf[qb][kc] = load_bf16x8(Q + base + (size_t)row * D + 16 * kc + 8 * half);
     }
+    // Retire the Q loads before the K/V pipeline starts, so every later vmcnt wait counts
+    // only the K/V stage loads.
+    wait_vmcnt<0>();
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-    const int nt = (kv_end + BN - 1) / BN;
+    const int nt = (kv_end + BK - 1) / BK;
+    // Sub-tiles this wave computes: causal waves stop at their own last row.
+    const int wave_nt = (wq0 >= N) ? 0 : (CAUSAL ? min(nt, (wq0 + RW - 1) / BK + 1) : nt);
 
-    u32x4 kst[NCH], vst[NCH];
-    auto gload = [&](int t) {
-        const int kv0 = t * BN;
+    // Per-thread byte offsets of the LDS-direct loads inside one sub-tile (fixed across tiles):
+    // LDS chunk g = j * NT + tid holds row g / CPR, logical chunk (g % CPR) ^ swz_row(row).
+    uint32_t voff[LPT];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-            if (kv0 + r < N) {
-                kst[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)(kv0 + r) * D + cc * 8);
-                vst[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)(kv0 + r) * D + cc * 8);
-            } else {
-                kst[i] = u32x4{0, 0, 0, 0};
-                vst[i] = u32x4{0, 0, 0, 0};
-            }
+    for (int j = 0; j < LPT; ++j) {
+        const int g = j * NT + tid, r = g / CPR, c = (g % CPR) ^ swz_row<D>(r);
+        voff[j] = (uint32_t)((r * D + c * 8) * 2);
+    }
+    const __bf16* Kh = K + base;
+    const __bf16* Vh = V + base;
+    // Enqueue sub-tile t into stage t % NS (= ST).  Tiles at or past N read zeros.
+    auto issue = [&](auto st, int t) {
+        constexpr int ST = decltype(st)::value;
+        const int kv0 = t * BK;
+        const uint32_t bytes = (uint32_t)max(0, N - kv0) * D * 2;
+        const i32x4 rk = make_rsrc(Kh + (size_t)min(kv0, N) * D, bytes);
+        const i32x4 rv = make_rsrc(Vh + (size_t)min(kv0, N) * D, bytes);
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            load_lds_b128(rk, lds_addr(&Ks[ST][(j * NT + wave * 64) * 8]), voff[j]);
+            load_lds_b128(rv, lds_addr(&Vs[ST][(j * NT + wave * 64) * 8]), voff[j]);
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-            *reinterpret_cast<u32x4*>(&Ks[buf][r * KST + cc * 8]) = kst[i];
-            *reinterpret_cast<u32x4*>(&Vs[buf][r * VST + cc * 8]) = vst[i];
-        }
-    };
 
-    f32x16 oacc[DB];
+    f32x16 oacc[QB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    float m_ref = kNegBig;  // log2-domain reference maximum of this row
-    float lsum = 0.f;       // this lane's share of the row sum (the other half holds the rest)
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1, kv0 = t * BN;
-        if (t + 1 < nt) gload(t + 1);
-
-        const bool active = (wq0 < N) && (!CAUSAL || kv0 <= wq0 + 31);  // wave-uniform
-        if (active) {
-            // S^T tile: rows = 64 keys (two 32-blocks), columns = the wave's 32 queries.
-            f32x16 s[2] = {f32x16{}, f32x16{}};
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int kc = 0; kc < DC; ++kc) {
+        for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
+    float m_ref[QB], lsum[QB];  // log2-domain reference max; this lane's share of the row sum
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = load_bf16x8(&Ks[buf][(32 * kb + l32) * KST + 16 * kc + 8 * half]);
-                    s[kb] = mfma_bf16(a, qf[kc], s[kb]);
-                }
-            }
-            // Masks: causal (key > query) on tiles that reach past the wave's first row,
-            // and keys beyond N on the ragged last tile.
-            const bool need_mask = CAUSAL ? (kv0 + BN - 1 > wq0) : (kv0 + BN > N);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-                        const bool dead = CAUSAL ? (key > myq) : (key >= N);
-                        if (dead) s[kb][r] = -INFINITY;
-                    }
-            }
-            // Row maximum of this tile (log2 domain).
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mt = mx * scale_log2;
-            if (__any(mt > m_ref + kRescaleSlack)) {
-                const float mn = fmaxf(m_ref, mt);
-                const float alpha = fast_exp2(m_ref - mn);
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-                m_ref = mn;
-            }
-            // P~ = exp2(s * scale * log2(e) - m_ref), summed and rounded to bf16 operands.
-            bf16x8 pb[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_ref));
-                    s[kb][r] = p;
-                    lsum += p;
-                }
-                pb[kb][0] = to_bf16x8(s[kb], 0);
-                pb[kb][1] = to_bf16x8(s[kb], 8);
-            }
-            // O^T += V^T P^T.  For P^T operand (kb, cc), lane l carries keys
-            // 32kb + 16cc + 4(l/32) + {0..3} and the same + 8; the transposed LDS read
-            // gives V^T rows d = 32db + l%32 at exactly those keys.
-            const int tr_row = 4 * half + ((lane & 15) >> 2);
-            const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const __bf16* vrow = &Vs[buf][(32 * kb + 16 * cc + tr_row) * VST + tr_col];
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 a = join_tr(lds_read_tr16(vrow + 32 * db),
-                                                 lds_read_tr16(vrow + 8 * VST + 32 * db));
-                        oacc[db] = mfma_bf16(a, pb[kb][cc], oacc[db]);
-                    }
-                }
-        }
-        if (t + 1 < nt) lstore(buf ^ 1);
-        __syncthreads();
+    for (int qb = 0; qb < QB; ++qb) {
+        m_ref[qb] = kNegBig;
+        lsum[qb] = 0.f;
     }
 
-    // Epilogue: O = acc / l, lse = m_ref * ln 2 + ln l.
-    lsum += swap_halves(lsum);
-    if (myq < N) {
-        const float inv = 1.0f / lsum;
-        __bf16* orow = O + base + (size_t)myq * D;
+    // LDS read addresses that depend only on the lane (stages and k-steps add immediates).
+    // K rows for the A operand of S^T: row l32, chunk 2kc + half (swizzled).
+    const __bf16* k_lane[DC];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int kc = 0; kc < DC; ++kc) k_lane[kc] = &Ks[0][swz<D>(l32, 16 * kc + 8 * half)];
+    // Transposed V reads: rows tr_row and tr_row + 8 (16 cc adds whole rows: the swizzle
+    // repeats every 16 rows), column 32 db + tr_col.
+    const int tr_row = 4 * half + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const __bf16* v_lane[2][DB];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                __bf16 w[4];
+    for (int db = 0; db < DB; ++db) {
+        v_lane[0][db] = &Vs[0][swz<D>(tr_row, 32 * db + tr_col)];
+        v_lane[1][db] = &Vs[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
+    }
+
+    // S^T of the sub-tile in stage ST for both query blocks: lane = query, register r =
+    // key 8(r/4) + 4 half + r%4.
+    auto scores = [&](auto st, f32x16 (&s)[QB]) {
+        constexpr int ST = decltype(st)::value;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = (__bf16)(oacc[db][4 * g + i] * inv);
-                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * half) = __builtin_bit_cast(u32x2, w);
+        for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < DC; ++kc) {
+            const bf16x8 a = load_bf16x8(k_lane[kc] + ST * STAGE);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb] = mfma_bf16(a, qf[qb][kc], s[qb]);
+        }
+    };
+    // Causal (key > query) or tail (key >= N) mask; only sub-tiles that need it call this.
+    auto mask = [&](int t, f32x16 (&s)[QB]) {
+        const int kv0 = t * BK;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int myq = wq0 + 32 * qb + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + 8 * (r / 4) + 4 * half + (r % 4);
+                if (CAUSAL ? (key > myq) : (key >= N)) s[qb][r] = -INFINITY;
             }
-        if (half == 0) LSE[(size_t)bh * N + myq] = m_ref * kLn2 + __logf(lsum);
+        }
+    };
+    auto needs_mask = [&](int t) { return CAUSAL ? (t * BK + BK - 1 > wq0) : (t * BK + BK > N); };
+    static_assert(BK % 32 == 0, "a sub-tile past the wave's rows must be fully masked");
+    static_assert(BK % 16 == 0, "stage bases must keep the 16-row swizzle period");
+    // Row max of S(t) and the (rare) raise of the reference max: O and l are rescaled by
+    // 2^(m_old - m_new) only when some row's max exceeds its reference by more than the slack.
+    auto raise_ref = [&](f32x16 (&s)[QB]) {
+        float mt[QB];
+        bool up = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
+            mx = fmaxf(mx, swap_halves(mx));
+            mt[qb] = mx * scale_log2;
+            up |= mt[qb] > m_ref[qb] + kRescaleSlack;
+        }
+        if (__any(up)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mn = fmaxf(m_ref[qb], mt[qb]);
+                const float alpha = fast_exp2(m_ref[qb] - mn);
+                lsum[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+                m_ref[qb] = mn;
+            }
+        }
+    };
+    // P(t) = 2^(S * scale * log2 e - m_ref), rounded to bf16 B operands (P^T, keys as in S^T).
+    auto probs = [&](f32x16 (&s)[QB], bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(fmaf(s[qb][r], scale_log2, -m_ref[qb]));
+            pb[qb][0] = to_bf16x8(s[qb], 0);
+            pb[qb][1] = to_bf16x8(s[qb], 8);
+        }
+    };
+    auto rowsum = [&](const f32x16 (&p)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                a += p[qb][r];
+                b += p[qb][r + 1];
+            }
+            lsum[qb] += a + b;
+        }
+    };
+    // O^T += V^T P^T for the sub-tile in stage ST: for k-step cc the B operand holds keys
+    // 16cc + 8(i/4) + 4 half + i%4, and the two transposed reads fetch V^T at exactly those
+    // keys (rows 16cc + tr_row and 16cc + tr_row + 8).
+    auto pv = [&](auto st, const bf16x8 (&pb)[QB][2]) {
+        constexpr int ST = decltype(st)::value;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int off = ST * STAGE + 16 * cc * D;
+                const bf16x8 a = join_tr(lds_read_tr16(v_lane[0][db] + off), lds_read_tr16(v_lane[1][db] + off));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma_bf16(a, pb[qb][cc], oacc[qb][db]);
+            }
+        }
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    static_assert(NS == 4, "the loop below is unrolled over four stages");
+
+    // Prologue: NS - 1 sub-tiles in flight, then S(0).
+    issue(S0{}, 0);
+    issue(S1{}, 1);
+    issue(S2{}, 2);
+    wait_vmcnt<(NS - 2) * LPS>();
+    __syncthreads();
+
+    f32x16 sa[QB], sb[QB];
+    if (wave_nt > 0) {
+        scores(S0{}, sa);
+        if (needs_mask(0)) mask(0, sa);
+        raise_ref(sa);
+    }
+
+    // One pipeline step on sub-tile i (stage CUR = i % NS): `cur` holds S(i) (masked,
+    // reference raised); leaves S(i+1) in `nxt`.  Every wave runs every step (barriers and
+    // loads are collective); the arithmetic is skipped past the wave's own last sub-tile.
+    // On that last sub-tile S(i+1) is still computed (its stage holds loaded data or zeros)
+    // but every key of it lies past the wave's rows or past N, so the mask clears it and
+    // it raises nothing.
+    // Region 1: the exponentials of S(i) overlap the MFMAs of S(i+1).  Region 2: the row
+    // sums of P(i) and the max of S(i+1) overlap the MFMAs of O += P(i) V(i).
+    auto step = [&](auto cur_st, int i, f32x16 (&cur)[QB], f32x16 (&nxt)[QB]) {
+        constexpr int CUR = decltype(cur_st)::value;
+        wait_vmcnt<(NS - 3) * LPS>();  // sub-tile i + 1 has landed (this wave's share)
+        __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
+        issue(std::integral_constant<int, (CUR + NS - 1) % NS>{}, i + NS - 1);
+        if (i >= wave_nt) return;
+        bf16x8 pb[QB][2];
+        probs(cur, pb);
+        scores(std::integral_constant<int, (CUR + 1) % NS>{}, nxt);
+        interleave_mfma<DC * QB, 0, 6>();
+        pin_regs(pb);  // keep the exponentials in region 1 (they would sink to their use)
+        if (needs_mask(i + 1)) mask(i + 1, nxt);
+        pv(cur_st, pb);
+        rowsum(cur);
+        raise_ref(nxt);
+    };
+    int i = 0;
+    for (; i + 3 < nt; i += 4) {
+        step(S0{}, i, sa, sb);
+        step(S1{}, i + 1, sb, sa);
+        step(S2{}, i + 2, sa, sb);
+        step(S3{}, i + 3, sb, sa);
+    }
+    if (i < nt) step(S0{}, i, sa, sb);
+    if (i + 1 < nt) step(S1{}, i + 1, sb, sa);
+    if (i + 2 < nt) step(S2{}, i + 2, sa, sb);
+
+    // Epilogue: O = acc / l, lse = m_ref ln 2 + ln l.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l = lsum[qb] + swap_halves(lsum[qb]);
+        const int myq = wq0 + 32 * qb + l32;
+        if (myq < N) {
+            const float inv = 1.0f / l;
+            __bf16* orow = O + base + (size_t)myq * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    __bf16 w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[qb][db][4 * g + e] * inv);
+                    *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * half) = __builtin_bit_cast(u32x2, w);
+                }
+            if (half == 0) LSE[(size_t)bh * N + myq] = m_ref[qb] * kLn2 + __logf(l);
+        }
     }
 }
 
@@ -320,12 +458,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int QB, bool CAUSAL>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t st) {
-    constexpr int BM = 32 * NW;
+    constexpr int BM = 32 * QB * NW;
     const int nqt = (a.N + BM - 1) / BM;
     const long long grid = (long long)nqt * a.B * a.H;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
                        a.N, nqt, a.scale * kLog2e);
     return hipGetLastError();
@@ -345,8 +483,8 @@ hipError_t launch_f32(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     if (a.dtype == kBF16) {
-        if (a.d == 128) return a.causal ? launch_bf16<128, 4, true>(a, st) : launch_bf16<128, 4, false>(a, st);
-        return a.causal ? launch_bf16<64, 4, true>(a, st) : launch_bf16<64, 4, false>(a, st);
+        if (a.d == 128) return a.causal ? launch_bf16<128, 4, 1, true>(a, st) : launch_bf16<128, 4, 1, false>(a, st);
+        return a.causal ? launch_bf16<64, 4, 1, true>(a, st) : launch_bf16<64, 4, 1, false>(a, st);
     }
     if (a.d == 128) return a.causal ? launch_f32<128, true>(a, st) : launch_f32<128, false>(a, st);
     return a.causal ? launch_f32<64, true>(a, st) : launch_f32<64, false>(a, st);
