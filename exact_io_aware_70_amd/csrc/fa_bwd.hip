@@ -17,6 +17,8 @@
 //   3. dQ:     one workgroup per query tile, each wave holding 32 queries, walking the key
 //              tiles (recomputes S and dP a second time instead of accumulating dQ with
 //              atomics).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -53,46 +55,56 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
 }
 
 // ------------------------------------------------------------------ bf16 dK / dV
-// Workgroup: NW waves x 32 keys.  Per step a 64-row query tile (Q, dO, lse, D) is staged
-// in LDS (double-buffered).  S = Q K^T and dP = dO V^T are computed with keys along the
-// lanes (C layout: lane = key, registers = queries), so P and dS feed the B operand of
-// dV^T += dO^T P and dK^T += Q^T dS directly; dO^T and Q^T come from transposed LDS reads.
+// Workgroup: NW waves, each holding 32 keys (K^T and V^T fragments as MFMA B operands and
+// the dK^T, dV^T accumulators in registers).  Query sub-tiles of 32 rows (Q, dO, lse, D)
+// stream through an NS-stage LDS ring filled by loads that write LDS directly; Q and dO
+// rows are XOR-swizzled exactly like the forward's K/V stages, so the row reads (A operands
+// of S and dP) and the transposed reads (dO^T, Q^T for dV and dK) are conflict-free.
+// S = Q K^T and dP = dO V^T come out with lane = key, register = query, so P and dS feed
+// the B operands of dV^T += dO^T P and dK^T += Q^T dS without any shuffle.
+// Query rows past N load as zeros with lse = D = 0: their P is 1 but multiplies zero dO
+// rows, and their dS = P (0 - 0) = 0, so they contribute nothing.
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2) {
-    constexpr int BNK = 32 * NW, BQ = 64, NT = NW * 64;
-    constexpr int ST = D + 8;
-    constexpr int DC = D / 16, DB = D / 32, CPR = D / 8;
-    constexpr int NCH = BQ * CPR / NT;
-    static_assert(NCH >= 1 && BQ * CPR % NT == 0, "tile / thread mismatch");
+    constexpr int BQ = 32;              // query rows per sub-tile
+    constexpr int NS = 4;               // LDS stages
+    constexpr int STAGE = BQ * D;       // bf16 elements per tensor per stage
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int NT = NW * 64;
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int LPT = BQ * CPR / NT;  // LDS-direct 16-byte loads per thread per tensor per sub-tile
+    constexpr int LPS = 2 * LPT + 2;    // per sub-tile: Q, dO, then lse and D (4 bytes per lane)
+    static_assert(LPT >= 1 && BQ * CPR % NT == 0, "tile / thread mismatch");
+    static_assert((NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
-    __shared__ __attribute__((aligned(16))) __bf16 dOs[2][BQ * ST];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
-    __shared__ __attribute__((aligned(16))) float del_s[2][BQ];
+    __shared__ __attribute__((aligned(1024))) __bf16 Qs[NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 dOs[NS][STAGE];
+    // lse and D rows of each stage; each 64-lane 4-byte load fills one 64-float row (lanes
+    // past the sub-tile read zeros into the unused upper half).
+    __shared__ __attribute__((aligned(256))) float LDs[NS][2][64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = L / nkt;
-    const int kt = L % nkt;  // causal: low key tiles see the most queries; they go first
-    const int k0 = kt * BNK, kw0 = k0 + wave * 32, mykey = kw0 + l32;
-    const size_t base = (size_t)bh * N * D;
-    const size_t rbase = (size_t)bh * N;
+    const int kt = L % nkt;              // causal: low key tiles see the most queries
+    const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wave, mykey = kw0 + l32;
+    const size_t base = (size_t)bh * N * D, rbase = (size_t)bh * N;
 
+    // K^T and V^T fragments (B operands): row mykey (clamped; results past N are not stored).
     bf16x8 kf[DC], vf[DC];
+    {
+        const int row = min(mykey, N - 1);
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) {
-        if (mykey < N) {
-            kf[kc] = load_bf16x8(K + base + (size_t)mykey * D + 16 * kc + 8 * half);
-            vf[kc] = load_bf16x8(V + base + (size_t)mykey * D + 16 * kc + 8 * half);
-        } else {
-            kf[kc] = bf16x8{};
-            vf[kc] = bf16x8{};
+        for (int kc = 0; kc < DC; ++kc) {
+            kf[kc] = load_bf16x8(K + base + (size_t)row * D + 16 * kc + 8 * half);
+            vf[kc] = load_bf16x8(V + base + (size_t)row * D + 16 * kc + 8 * half);
         }
     }
+    wait_vmcnt<0>();
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -100,99 +112,113 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
         dv[db] = f32x16{};
     }
 
-    const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
-    const int nsteps = (N - q_begin + BQ - 1) / BQ;
+    const int t_begin = CAUSAL ? k0 / BQ : 0;   // first query sub-tile any key here can see
+    const int nsteps = (N + BQ - 1) / BQ - t_begin;
+    const int wave_first = CAUSAL ? kw0 / BQ : 0;
+    const bool wave_live = kw0 < N;
 
-    u32x4 qst[NCH], ost[NCH];
-    float lse_r = 0.f, del_r = 0.f;
-    auto gload = [&](int s) {
-        const int qs0 = q_begin + s * BQ;
+    uint32_t voff[LPT];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-            if (qs0 + r < N) {
-                qst[i] = *reinterpret_cast<const u32x4*>(Q + base + (size_t)(qs0 + r) * D + cc * 8);
-                ost[i] = *reinterpret_cast<const u32x4*>(dO + base + (size_t)(qs0 + r) * D + cc * 8);
-            } else {
-                qst[i] = u32x4{0, 0, 0, 0};
-                ost[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-        if (tid < BQ) {
-            // Rows past N: lse = +inf makes their P exactly 0, and D = 0 their dS.
-            lse_r = (qs0 + tid < N) ? LSE[rbase + qs0 + tid] * kLog2e : INFINITY;
-            del_r = (qs0 + tid < N) ? Delta[rbase + qs0 + tid] : 0.f;
-        }
-    };
-    auto lstore = [&](int buf) {
+    for (int j = 0; j < LPT; ++j) {
+        const int g = j * NT + tid, r = g / CPR, c = (g % CPR) ^ swz_row<D>(r);
+        voff[j] = (uint32_t)((r * D + c * 8) * 2);
+    }
+    // Sub-tile t of the query range into stage ST.  Rows at or past N read zeros.  Every
+    // wave writes the (identical) lse / D rows, so each wave issues the same loads.
+    auto issue = [&](auto st, int t) {
+        constexpr int ST = decltype(st)::value;
+        const int q0 = t * BQ;
+        const uint32_t rows = (uint32_t)max(0, N - q0);
+        const i32x4 rq = make_rsrc(Q + base + (size_t)min(q0, N) * D, rows * D * 2);
+        const i32x4 ro = make_rsrc(dO + base + (size_t)min(q0, N) * D, rows * D * 2);
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-            *reinterpret_cast<u32x4*>(&Qs[buf][r * ST + cc * 8]) = qst[i];
-            *reinterpret_cast<u32x4*>(&dOs[buf][r * ST + cc * 8]) = ost[i];
+        for (int j = 0; j < LPT; ++j) {
+            load_lds_b128(rq, lds_addr(&Qs[ST][(j * NT + wave * 64) * 8]), voff[j]);
+            load_lds_b128(ro, lds_addr(&dOs[ST][(j * NT + wave * 64) * 8]), voff[j]);
         }
-        if (tid < BQ) {
-            lse_s[buf][tid] = lse_r;
-            del_s[buf][tid] = del_r;
-        }
+        const i32x4 rl = make_rsrc(LSE + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
+        const i32x4 rd = make_rsrc(Delta + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
+        load_lds_b32(rl, lds_addr(&LDs[ST][0][0]), (uint32_t)(lane * 4));
+        load_lds_b32(rd, lds_addr(&LDs[ST][1][0]), (uint32_t)(lane * 4));
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
+    // LDS read addresses that depend only on the lane.
+    const __bf16* r_lane[DC];  // Q / dO rows (A operands of S and dP): row l32, chunk 2kc + half
+#pragma unroll
+    for (int kc = 0; kc < DC; ++kc) r_lane[kc] = &Qs[0][swz<D>(l32, 16 * kc + 8 * half)];
     const int tr_row = 4 * half + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const __bf16* t_lane[2][DB];  // transposed reads (dO^T, Q^T): rows tr_row, tr_row + 8
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        t_lane[0][db] = &Qs[0][swz<D>(tr_row, 32 * db + tr_col)];
+        t_lane[1][db] = &Qs[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
+    }
+    constexpr int DO_OFF = (int)(sizeof(Qs) / sizeof(__bf16));  // dOs follows Qs in the same layout
 
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1, qs0 = q_begin + s * BQ;
-        if (s + 1 < nsteps) gload(s + 1);
-        if (kw0 < N) {
+    auto step = [&](auto st, int i) {
+        constexpr int ST = decltype(st)::value;
+        wait_vmcnt<(NS - 2) * LPS>();  // sub-tile i has landed (this wave's share) ...
+        __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
+        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, t_begin + i + NS - 1);
+        const int t = t_begin + i;
+        if (!wave_live || t < wave_first) return;
+        // S = Q K^T and dP = dO V^T: lane = key, register r = query 8(r/4) + 4 half + r%4.
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int qb0 = qs0 + 32 * qb;
-                if (CAUSAL && qb0 + 31 < kw0) continue;  // every query of the block precedes every key
-                f32x16 sacc = f32x16{}, pacc = f32x16{};
+        for (int kc = 0; kc < DC; ++kc) {
+            sacc = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE), kf[kc], sacc);
+            pacc = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE + DO_OFF), vf[kc], pacc);
+        }
+        const bool diag = CAUSAL && t == wave_first;
 #pragma unroll
-                for (int kc = 0; kc < DC; ++kc) {
-                    const int off = (32 * qb + l32) * ST + 16 * kc + 8 * half;
-                    sacc = mfma_bf16(load_bf16x8(&Qs[buf][off]), kf[kc], sacc);
-                    pacc = mfma_bf16(load_bf16x8(&dOs[buf][off]), vf[kc], pacc);
-                }
-                // lane = key, register r = query 32qb + 8(r/4) + 4half + r%4.
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&LDs[ST][0][8 * g + 4 * half]);
+            const f32x4 del4 = *reinterpret_cast<const f32x4*>(&LDs[ST][1][8 * g + 4 * half]);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int ql = 32 * qb + 8 * g + 4 * half;
-                    const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&lse_s[buf][ql]);
-                    const f32x4 del4 = *reinterpret_cast<const f32x4*>(&del_s[buf][ql]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float p = fast_exp2(fmaf(sacc[4 * g + i], scale_log2, -lse4[i]));
-                        if (CAUSAL && mykey > qs0 + ql + i) p = 0.f;
-                        sacc[4 * g + i] = p;
-                        pacc[4 * g + i] = p * (pacc[4 * g + i] - del4[i]);
-                    }
-                }
-                const bf16x8 pb[2] = {to_bf16x8(sacc, 0), to_bf16x8(sacc, 8)};
-                const bf16x8 sb[2] = {to_bf16x8(pacc, 0), to_bf16x8(pacc, 8)};
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int row = (32 * qb + 16 * cc + tr_row) * ST + tr_col;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 a_do = join_tr(lds_read_tr16(&dOs[buf][row + 32 * db]),
-                                                    lds_read_tr16(&dOs[buf][row + 8 * ST + 32 * db]));
-                        dv[db] = mfma_bf16(a_do, pb[cc], dv[db]);
-                        const bf16x8 a_q = join_tr(lds_read_tr16(&Qs[buf][row + 32 * db]),
-                                                   lds_read_tr16(&Qs[buf][row + 8 * ST + 32 * db]));
-                        dk[db] = mfma_bf16(a_q, sb[cc], dk[db]);
-                    }
-                }
+            for (int e = 0; e < 4; ++e) {
+                float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -lse4[e] * kLog2e));
+                if (diag && mykey > t * BQ + 8 * g + 4 * half + e) p = 0.f;
+                sacc[4 * g + e] = p;
+                pacc[4 * g + e] = p * (pacc[4 * g + e] - del4[e]);
             }
         }
-        if (s + 1 < nsteps) lstore(buf ^ 1);
-        __syncthreads();
+        const bf16x8 pb[2] = {to_bf16x8(sacc, 0), to_bf16x8(sacc, 8)};
+        const bf16x8 sb[2] = {to_bf16x8(pacc, 0), to_bf16x8(pacc, 8)};
+        // dV^T += dO^T P, dK^T += Q^T dS: for k-step cc the B operands hold queries
+        // 16cc + 8(i/4) + 4 half + i%4; the transposed reads fetch rows 16cc + tr_row (+8).
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int off = ST * STAGE + 16 * cc * D;
+                const bf16x8 a_do = join_tr(lds_read_tr16(t_lane[0][db] + off + DO_OFF),
+                                            lds_read_tr16(t_lane[1][db] + off + DO_OFF));
+                dv[db] = mfma_bf16(a_do, pb[cc], dv[db]);
+                const bf16x8 a_q = join_tr(lds_read_tr16(t_lane[0][db] + off), lds_read_tr16(t_lane[1][db] + off));
+                dk[db] = mfma_bf16(a_q, sb[cc], dk[db]);
+            }
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    static_assert(NS == 4, "the loop below is unrolled over four stages");
+    issue(S0{}, t_begin);
+    issue(S1{}, t_begin + 1);
+    issue(S2{}, t_begin + 2);
+    int i = 0;
+    for (; i + 3 < nsteps; i += 4) {
+        step(S0{}, i);
+        step(S1{}, i + 1);
+        step(S2{}, i + 2);
+        step(S3{}, i + 3);
     }
+    if (i < nsteps) step(S0{}, i);
+    if (i + 1 < nsteps) step(S1{}, i + 1);
+    if (i + 2 < nsteps) step(S2{}, i + 2);
+    wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the wave ends
 
     if (mykey < N) {
         __bf16* dkrow = dK + base + (size_t)mykey * D;
@@ -203,9 +229,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
             for (int g = 0; g < 4; ++g) {
                 __bf16 wk[4], wv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    wk[i] = (__bf16)(dk[db][4 * g + i] * scale);
-                    wv[i] = (__bf16)dv[db][4 * g + i];
+                for (int e = 0; e < 4; ++e) {
+                    wk[e] = (__bf16)(dk[db][4 * g + e] * scale);
+                    wv[e] = (__bf16)dv[db][4 * g + e];
                 }
                 const int col = 32 * db + 8 * g + 4 * half;
                 *reinterpret_cast<u32x2*>(dkrow + col) = __builtin_bit_cast(u32x2, wk);
@@ -215,125 +241,141 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_bf16_kernel(
 }
 
 // ------------------------------------------------------------------ bf16 dQ
-// Workgroup: NW waves x 32 queries, K/V tiles of 64 keys double-buffered in LDS.  Like
-// the forward: S^T = K Q^T and dP^T = V dO^T put one query per lane, so lse and D are
-// per-lane scalars and dS^T feeds dQ^T += K^T dS^T (K^T by transposed LDS reads).
+// Workgroup: NW waves x 32 queries (Q^T and dO^T fragments as B operands, the dQ^T
+// accumulator in registers); K/V sub-tiles of 32 keys stream through the same swizzled
+// NS-stage LDS ring as the forward.  S^T = K Q^T and dP^T = V dO^T put one query per lane,
+// so lse and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T (K^T by transposed
+// reads).  This recomputes S and dP instead of accumulating dQ with atomics.
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2) {
-    constexpr int BM = 32 * NW, BN = 64, NT = NW * 64;
-    constexpr int KST = D + 16;  // K is read both row-wise and transposed
-    constexpr int VST = D + 8;
-    constexpr int DC = D / 16, DB = D / 32, CPR = D / 8;
-    constexpr int NCH = BN * CPR / NT;
-    static_assert(NCH >= 1 && BN * CPR % NT == 0, "tile / thread mismatch");
+    constexpr int BK = 32, NS = 4, STAGE = BK * D, CPR = D / 8, NT = NW * 64;
+    constexpr int BM = 32 * NW, DC = D / 16, DB = D / 32;
+    constexpr int LPT = BK * CPR / NT;
+    constexpr int LPS = 2 * LPT;
+    static_assert(LPT >= 1 && BK * CPR % NT == 0, "tile / thread mismatch");
+    static_assert((NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KST];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VST];
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs[NS][STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = L / nqt;
-    const int q0 = (nqt - 1 - (L % nqt)) * BM;
+    const int q0 = (nqt - 1 - (L % nqt)) * BM;  // heaviest (causal) tiles first
     const size_t base = (size_t)bh * N * D;
-    const int wq0 = q0 + wave * 32, myq = wq0 + l32;
+    const int wq0 = q0 + 32 * wave, myq = wq0 + l32;
 
     bf16x8 qf[DC], of[DC];
+    {
+        const int row = min(myq, N - 1);
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) {
-        if (myq < N) {
-            qf[kc] = load_bf16x8(Q + base + (size_t)myq * D + 16 * kc + 8 * half);
-            of[kc] = load_bf16x8(dO + base + (size_t)myq * D + 16 * kc + 8 * half);
-        } else {
-            qf[kc] = bf16x8{};
-            of[kc] = bf16x8{};
+        for (int kc = 0; kc < DC; ++kc) {
+            qf[kc] = load_bf16x8(Q + base + (size_t)row * D + 16 * kc + 8 * half);
+            of[kc] = load_bf16x8(dO + base + (size_t)row * D + 16 * kc + 8 * half);
         }
     }
-    const float lse_l = (myq < N) ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
-    const float del_l = (myq < N) ? Delta[(size_t)bh * N + myq] : 0.f;
+    // Rows past N: lse = +inf makes their P exactly 0 (they are not stored either).
+    const float lse2 = (myq < N) ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
+    const float del = (myq < N) ? Delta[(size_t)bh * N + myq] : 0.f;
+    wait_vmcnt<0>();
 
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-    const int nt = (kv_end + BN - 1) / BN;
+    const int nt = (kv_end + BK - 1) / BK;
+    const int wave_nt = (wq0 >= N) ? 0 : (CAUSAL ? min(nt, (wq0 + 31) / BK + 1) : nt);
 
-    u32x4 kst[NCH], vst[NCH];
-    auto gload = [&](int t) {
-        const int kv0 = t * BN;
+    uint32_t voff[LPT];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-            if (kv0 + r < N) {
-                kst[i] = *reinterpret_cast<const u32x4*>(K + base + (size_t)(kv0 + r) * D + cc * 8);
-                vst[i] = *reinterpret_cast<const u32x4*>(V + base + (size_t)(kv0 + r) * D + cc * 8);
-            } else {
-                kst[i] = u32x4{0, 0, 0, 0};
-                vst[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
+    for (int j = 0; j < LPT; ++j) {
+        const int g = j * NT + tid, r = g / CPR, c = (g % CPR) ^ swz_row<D>(r);
+        voff[j] = (uint32_t)((r * D + c * 8) * 2);
+    }
+    auto issue = [&](auto st, int t) {
+        constexpr int ST = decltype(st)::value;
+        const int kv0 = t * BK;
+        const uint32_t bytes = (uint32_t)max(0, N - kv0) * D * 2;
+        const i32x4 rk = make_rsrc(K + base + (size_t)min(kv0, N) * D, bytes);
+        const i32x4 rv = make_rsrc(V + base + (size_t)min(kv0, N) * D, bytes);
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * NT, r = c / CPR, cc = c % CPR;
-            *reinterpret_cast<u32x4*>(&Ks[buf][r * KST + cc * 8]) = kst[i];
-            *reinterpret_cast<u32x4*>(&Vs[buf][r * VST + cc * 8]) = vst[i];
+        for (int j = 0; j < LPT; ++j) {
+            load_lds_b128(rk, lds_addr(&Ks[ST][(j * NT + wave * 64) * 8]), voff[j]);
+            load_lds_b128(rv, lds_addr(&Vs[ST][(j * NT + wave * 64) * 8]), voff[j]);
         }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
+    const __bf16* r_lane[DC];  // K / V rows (A operands of S^T and dP^T)
+#pragma unroll
+    for (int kc = 0; kc < DC; ++kc) r_lane[kc] = &Ks[0][swz<D>(l32, 16 * kc + 8 * half)];
+    constexpr int V_OFF = (int)(sizeof(Ks) / sizeof(__bf16));  // Vs follows Ks in the same layout
     const int tr_row = 4 * half + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1, kv0 = t * BN;
-        if (t + 1 < nt) gload(t + 1);
-        const bool active = (wq0 < N) && (!CAUSAL || kv0 <= wq0 + 31);
-        if (active) {
-            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    const __bf16* t_lane[2][DB];  // K^T by transposed reads: rows tr_row, tr_row + 8
 #pragma unroll
-            for (int kc = 0; kc < DC; ++kc)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = mfma_bf16(load_bf16x8(&Ks[buf][(32 * kb + l32) * KST + 16 * kc + 8 * half]), qf[kc], s[kb]);
-                    dp[kb] = mfma_bf16(load_bf16x8(&Vs[buf][(32 * kb + l32) * VST + 16 * kc + 8 * half]), of[kc], dp[kb]);
-                }
-            bf16x8 sb[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-                    float p = fast_exp2(fmaf(s[kb][r], scale_log2, -lse_l));
-                    if (CAUSAL ? (key > myq) : (key >= N)) p = 0.f;
-                    dp[kb][r] = p * (dp[kb][r] - del_l);
-                }
-                sb[kb][0] = to_bf16x8(dp[kb], 0);
-                sb[kb][1] = to_bf16x8(dp[kb], 8);
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const __bf16* krow = &Ks[buf][(32 * kb + 16 * cc + tr_row) * KST + tr_col];
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 a = join_tr(lds_read_tr16(krow + 32 * db), lds_read_tr16(krow + 8 * KST + 32 * db));
-                        dq[db] = mfma_bf16(a, sb[kb][cc], dq[db]);
-                    }
-                }
-        }
-        if (t + 1 < nt) lstore(buf ^ 1);
-        __syncthreads();
+    for (int db = 0; db < DB; ++db) {
+        t_lane[0][db] = &Ks[0][swz<D>(tr_row, 32 * db + tr_col)];
+        t_lane[1][db] = &Ks[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
     }
+
+    auto step = [&](auto st, int i) {
+        constexpr int ST = decltype(st)::value;
+        wait_vmcnt<(NS - 2) * LPS>();
+        __syncthreads();
+        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, i + NS - 1);
+        if (i >= wave_nt) return;
+        const int kv0 = i * BK;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < DC; ++kc) {
+            s = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE), qf[kc], s);
+            dp = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE + V_OFF), of[kc], dp);
+        }
+        const bool need_mask = CAUSAL ? (kv0 + BK - 1 > wq0) : (kv0 + BK > N);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+            if (need_mask) {
+                const int key = kv0 + 8 * (r / 4) + 4 * half + (r % 4);
+                if (CAUSAL ? (key > myq) : (key >= N)) p = 0.f;
+            }
+            dp[r] = p * (dp[r] - del);
+        }
+        const bf16x8 sb[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int off = ST * STAGE + 16 * cc * D;
+                const bf16x8 a = join_tr(lds_read_tr16(t_lane[0][db] + off), lds_read_tr16(t_lane[1][db] + off));
+                dq[db] = mfma_bf16(a, sb[cc], dq[db]);
+            }
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    static_assert(NS == 4, "the loop below is unrolled over four stages");
+    issue(S0{}, 0);
+    issue(S1{}, 1);
+    issue(S2{}, 2);
+    int i = 0;
+    for (; i + 3 < nt; i += 4) {
+        step(S0{}, i);
+        step(S1{}, i + 1);
+        step(S2{}, i + 2);
+        step(S3{}, i + 3);
+    }
+    if (i < nt) step(S0{}, i);
+    if (i + 1 < nt) step(S1{}, i + 1);
+    if (i + 2 < nt) step(S2{}, i + 2);
+    wait_vmcnt<0>();
 
     if (myq < N) {
         __bf16* row = dQ + base + (size_t)myq * D;
@@ -343,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_bf16_kernel(
             for (int g = 0; g < 4; ++g) {
                 __bf16 w[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = (__bf16)(dq[db][4 * g + i] * scale);
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(dq[db][4 * g + e] * scale);
                 *reinterpret_cast<u32x2*>(row + 32 * db + 8 * g + 4 * half) = __builtin_bit_cast(u32x2, w);
             }
     }

@@ -98,6 +98,11 @@ __device__ __forceinline__ void load_lds_b128(i32x4 rsrc, uint32_t lds_base, uin
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
+// 4 bytes per lane from rsrc + voffset straight into LDS at lds_base + 4 l (see load_lds_b128).
+__device__ __forceinline__ void load_lds_b32(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(lds_base) : "memory");
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -127,6 +132,27 @@ __device__ __forceinline__ void pin_regs(bf16x8 (&v)[A][B]) {
     for (int a = 0; a < A; ++a)
 #pragma unroll
         for (int b = 0; b < B; ++b) asm volatile("" : "+v"(v[a][b]));
+}
+
+// LDS swizzle: row r of a stage stores its logical 16-byte chunk c at slot c ^ swz_row(r).
+// gfx950's LDS serves 256 bytes per clock to 128-bit reads (64 banks) and 128 bytes per
+// clock to the transposed 64-bit reads.  The K reads of the S^T product fetch one chunk
+// from 16 consecutive rows per 16 lanes, so the 16 rows must land in 16 different 16-byte
+// bank groups; the transposed V reads fetch two chunks from each of 4 consecutive rows per
+// 16 lanes, and run at full rate when those 8 pieces fill one aligned 128-byte span.
+//   D = 128 (256-byte rows): f(r) = (2r mod 8) | (r/4 mod 2) | (r mod 16 >= 8 ? 8 : 0)
+//   D = 64 (128-byte rows, two per 256 bytes): the same idea on row pairs.
+template <int D>
+__device__ __forceinline__ int swz_row(int r) {
+    if constexpr (D == 128) return ((2 * r) & 7) | ((r >> 2) & 1) | (r & 8);
+    const int x = (r >> 1) & 7;
+    return 2 * (x & 3) + ((x >> 2) & 1);
+}
+
+// Element index of (row, col) inside a swizzled stage (col a multiple of 4).
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * D + (((col >> 3) ^ swz_row<D>(row)) << 3) + (col & 7);
 }
 
 // Map a linear workgroup id to a logical one so that consecutive logical ids land on the
