@@ -1,22 +1,31 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--copy-mib M] [--workload NAME]
 
 One step = the whole hot path over one batch: fa_fwd (tiled online-softmax forward,
-writing O and lse) followed by fa_bwd (delta, dK/dV and dQ by recomputation) for the
-upstream gradient dO.  Inputs are seeded synthetic Gaussians already resident in HBM.
-The default workload is the bf16 causal forward stress case: B=4, H=32, N=8192, d=128,
-Q drawn x3, scale 1/sqrt(d).
+writing O and lse) followed by fa_bwd (D = rowsum(dO * O), dK/dV and dQ by recomputation)
+for the upstream gradient dO.  Inputs are seeded synthetic Gaussians already resident in
+HBM.  The default workload is the bf16 causal stress case: B=4, H=32, N=8192, d=128, Q
+drawn x3, scale 1/sqrt(d).
 
 FLOPs follow the metric: forward 4 B H N^2 d, halved for causal; the backward counts its
-five products, 10 B H N^2 d, halved for causal (the dQ kernel's recomputation is not
-counted).  `value` = step FLOPs / wall time per step.  The JSON line also carries the
-forward and backward separately (HIP events on the launch stream), the roofline of the
-dominant kernel, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+five products, 10 B H N^2 d, halved for causal (the dQ kernel's recomputation of S and dP
+is not counted).  `value` = step FLOPs / wall time per step.
+
+Every kernel is timed live with HIP events recorded on the launch stream (fa_bwd_timed
+records them between its own launches).  `roofline` is the dominant kernel's: its
+algorithmic units per launch over its average duration, against the MI355X peak for its
+bound.  `traffic` comes from the committed rocprofv3 counter summary
+(profiles/hbm_traffic_<workload>.txt, made by --summarize-pmc) and is null when the kernel
+sources have changed since those counters were taken.  `cpu_baseline` is the fp64 oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +38,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+KERNEL_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd.hip", "exact_io_aware_70_amd/csrc/fa_bwd.hip",
+                  "exact_io_aware_70_amd/csrc/fa_device.h"]
 
 
 def parse():
@@ -42,12 +53,109 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=0,
                    help="before the steps, copy this many MiB once with a plain device copy: the reference "
                         "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM byte counts")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, both with "
+                        "--copy-mib) into profiles/hbm_traffic_<workload>.txt, then exit")
     return p.parse_args()
 
 
 def flops(B, H, N, d, causal):
     f = 0.5 if causal else 1.0
     return 4.0 * B * H * N * N * d * f, 10.0 * B * H * N * N * d * f
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_table(dtype, B, H, N, d, causal):
+    """Algorithmic units per launch of each kernel of one step (name -> (bound, units, unit))."""
+    cf = 0.5 if causal else 1.0
+    elt = 2 if dtype == "bf16" else 4
+    sfx = "bf16" if dtype == "bf16" else "f32"
+    n2d = B * H * N * N * d * cf
+    return {
+        # two products (S = Q K^T, O = P V), 2 N^2 d flops each per head
+        f"fwd_{sfx}_kernel": ("mfma", 4.0 * n2d, "flop"),
+        # reads O and dO once, writes one float per row
+        "delta_kernel": ("hbm", 2.0 * B * H * N * d * elt + 4.0 * B * H * N, "byte"),
+        # four products: S, dP, dV += P^T dO, dK += dS^T Q
+        f"dkdv_{sfx}_kernel": ("mfma", 8.0 * n2d, "flop"),
+        # three products: S and dP (recomputed) and dQ += dS K
+        f"dq_{sfx}_kernel": ("mfma", 6.0 * n2d, "flop"),
+    }
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+
+
+def load_traffic(workload):
+    """Measured HBM bytes per launch from the committed counter summary, if still current."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_sha256") != sources_digest():
+        return None  # the kernels changed since the counters were taken
+    return data["kernels"]
+
+
+def summarize_pmc(args):
+    """Average FETCH_SIZE / WRITE_SIZE per dispatch of each kernel, scaled by the copy kernel."""
+    def read(dirname, counter):
+        per = {}
+        for dp, _, files in os.walk(dirname):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    with open(os.path.join(dp, fn)) as f:
+                        for r in csv.DictReader(f):
+                            if r["Counter_Name"] != counter:
+                                continue
+                            key = (r["Dispatch_Id"], r["Kernel_Name"])
+                            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return per
+
+    fetch, write = read(args.summarize_pmc[0], "FETCH_SIZE"), read(args.summarize_pmc[1], "WRITE_SIZE")
+    copy_bytes = args.copy_mib * (1 << 20)
+
+    def calib(per):
+        vals = [v for (_, name), v in per.items() if "copyBuffer" in name]
+        if not vals or copy_bytes <= 0:
+            raise SystemExit("no copy kernel in the counter runs (run them with --copy-mib)")
+        return copy_bytes / (vals[0] * 1024.0)
+
+    ff, fw = calib(fetch), calib(write)
+    names = ["fwd_bf16_kernel", "fwd_f32_kernel", "delta_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
+             "dq_bf16_kernel", "dq_f32_kernel"]
+    out = {}
+    for short in names:
+        fv = [v for (_, n), v in fetch.items() if short in n]
+        wv = [v for (_, n), v in write.items() if short in n]
+        if fv and wv:
+            fb = sum(fv) / len(fv) * 1024.0 * ff
+            wb = sum(wv) / len(wv) * 1024.0 * fw
+            out[short] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes": round(fb + wb),
+                          "dispatches": len(fv)}
+    data = {"workload": args.workload, "source_sha256": sources_digest(),
+            "fetch_scale": ff, "write_scale": fw, "copy_mib": args.copy_mib,
+            "commands": [f"rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -- python3 bench.py --steps 1 --warmup 1 "
+                         f"--no-cpu-baseline --copy-mib {args.copy_mib} --workload {args.workload}",
+                         f"rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -- python3 bench.py --steps 1 --warmup 1 "
+                         f"--no-cpu-baseline --copy-mib {args.copy_mib} --workload {args.workload}",
+                         f"python3 bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR> --copy-mib {args.copy_mib} "
+                         f"--workload {args.workload}"],
+            "kernels": out}
+    os.makedirs(os.path.dirname(traffic_file(args.workload)), exist_ok=True)
+    with open(traffic_file(args.workload), "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps(data, indent=1))
 
 
 def cpu_baseline(case, causal, heads):
@@ -59,22 +167,30 @@ def cpu_baseline(case, causal, heads):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    sl = (slice(0, 1), slice(0, heads))
-    q, k, v, do = (case[n]["values"][sl] for n in ("q", "k", "v", "do"))
-    t0 = time.perf_counter()
-    oracle.forward(q, k, v, case["scale"], causal)
-    oracle.backward(q, k, v, do, case["scale"], causal)
-    dt = time.perf_counter() - t0
-    B, H, N, d = q.shape
-    ff, fb = flops(B, H, N, d, causal)
-    return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of {case['shape'][0] * case['shape'][1]} heads (b=0), full N={N}, d={d}: "
-                      f"fp64 forward + backward with explicit S and P, {dt:.1f} s",
-            "seconds": round(dt, 3)}
+    B0, H0 = case["shape"][:2]
+    heads = min(heads, B0 * H0)
+    sel = [(b, h) for b in range(B0) for h in range(H0)][:heads]
+    t_total = 0.0
+    for b, h in sel:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        q, k, v, do = (case[n]["values"][sl] for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, case["scale"], causal)
+        oracle.backward(q, k, v, do, case["scale"], causal)
+        t_total += time.perf_counter() - t0
+    _, _, N, d = case["shape"]
+    ff, fb = flops(1, heads, N, d, causal)
+    return {"value": round((ff + fb) / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {B0 * H0} heads, full N={N}, d={d}: fp64 forward + backward with explicit S and P "
+                      f"({t_total:.1f} s); same flop formula as value",
+            "seconds": round(t_total, 3)}
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(heads shard across GPUs with no exchange, so one GPU runs one share).", file=sys.stderr)
@@ -104,16 +220,15 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d, code), dtype=torch.uint8, device=dev)
     sc = case["scale"]
     stream = torch.cuda.current_stream(dev)
+    kinds = kernel_table(case["dtype"], B, H, N, d, causal)
+    knames = list(kinds)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=sc, causal=causal, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=sc, causal=causal, workspace=ws, stream=stream,
+                  events=None if ev is None else ev[1:])
 
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20)
@@ -128,7 +243,12 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ev[0]: before fa_fwd; ev[1..4]: recorded by fa_bwd_timed before its three launches and after.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + fa.FA_BWD_LAUNCHES)]
+              for _ in range(args.steps)]
+    for ev in events:  # create the underlying events before the timed region
+        for e in ev:
+            e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -136,25 +256,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    # fwd = ev0 -> ev1 (fa_fwd is one launch); then delta, dK/dV, dQ between ev1..ev4.
+    per = {name: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, name in enumerate(knames)}
+    avg = {name: float(np.mean(ts)) for name, ts in per.items()}
     ms_step = wall * 1e3 / args.steps
     ff, fb = flops(B, H, N, d, causal)
-    fwd_avg, bwd_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
-    fwd_tf, bwd_tf = ff / (fwd_avg * 1e-3) / 1e12, fb / (bwd_avg * 1e-3) / 1e12
+    fwd_ms = avg[knames[0]]
+    bwd_ms = sum(avg[n] for n in knames[1:])
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if case["dtype"] == "bf16" else PEAK_F32_TFLOPS
-    elt = 2 if case["dtype"] == "bf16" else 4
-    tensor_bytes = B * H * N * d * elt
+    traffic = load_traffic(args.workload)
 
-    # Dominant kernel: the forward kernel is one launch per fa_fwd, so its average launch
-    # duration is the fwd event interval.  Its algorithmic units: 4 B H N^2 d (x1/2 causal)
-    # FLOPs; its compulsory bytes: Q, K, V read and O written once, lse written.
-    roofline = {"kernel": "fwd_bf16_kernel" if code == fa.FA_BF16 else "fwd_f32_kernel",
-                "bound": "mfma", "achieved": round(fwd_tf, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(fwd_tf / peak, 4), "traffic": None,
-                "launch_ms": round(fwd_avg, 4),
-                "compulsory_bytes": 4 * tensor_bytes + 4 * B * H * N}
+    kernels = {}
+    for name in knames:
+        bound, units, unit = kinds[name]
+        rate = units / (avg[name] * 1e-3)
+        if unit == "flop":
+            ach, pk, u = rate / 1e12, peak, "TFLOP/s"
+        else:
+            ach, pk, u = rate / 1e9, PEAK_HBM_GBS, "GB/s"
+        tb = traffic.get(name, {}).get("bytes") if traffic else None
+        kernels[name] = {"ms": round(avg[name], 4), "ms_min": round(min(per[name]), 4), "bound": bound,
+                         "achieved": round(ach, 2), "peak": pk, "unit": u, "frac": round(ach / pk, 4),
+                         "units_per_launch": units, "traffic": tb}
+    dom = max(knames, key=lambda n: avg[n])
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],
+                "unit": kd["unit"], "frac": kd["frac"], "traffic": kd["traffic"], "launch_ms": kd["ms"]}
 
     out = {
         "metric": "attention fwd/bwd TFLOP/s (4*B*H*N^2*d fwd, 10*B*H*N^2*d bwd, causal halved)",
@@ -172,11 +300,12 @@ def main():
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
                    "pass": "fwd+bwd", "step_flops": ff + fb},
         "pct_peak": round(100 * value / peak, 2),
-        "fwd": {"ms": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(fwd_tf, 2),
-                "pct_peak": round(100 * fwd_tf / peak, 2), "flops": ff},
-        "bwd": {"ms": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4), "tflops": round(bwd_tf, 2),
-                "pct_peak": round(100 * bwd_tf / peak, 2), "flops": fb,
-                "tflops_literal_4x": round(fb * 0.4 / (bwd_avg * 1e-3) / 1e12, 2)},
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * ff / (fwd_ms * 1e-3) / 1e12 / peak, 2), "flops": ff},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(fb / (bwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * fb / (bwd_ms * 1e-3) / 1e12 / peak, 2), "flops": fb,
+                "tflops_literal_4x": round(fb * 0.4 / (bwd_ms * 1e-3) / 1e12, 2)},
+        "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -16,11 +16,12 @@ import math
 import os
 
 __all__ = ["FAError", "library_path", "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_size",
-           "fa_status_string", "fa_version", "FA_OK", "FA_F32", "FA_BF16"]
+           "fa_status_string", "fa_version", "FA_OK", "FA_F32", "FA_BF16", "FA_BWD_LAUNCHES"]
 
 FA_OK = 0
 FA_F32 = 0
 FA_BF16 = 1
+FA_BWD_LAUNCHES = 3  # kernel launches per fa_bwd call: D, dK/dV, dQ
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -55,6 +56,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp,
+                                 ctypes.POINTER(vp)]
+    lib.fa_bwd_timed.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -130,11 +134,14 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None):
 
 
 def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=False,
-           workspace=None, stream=None):
+           workspace=None, stream=None, events=None):
     """Backward pass: returns (dq, dk, dv) for the loss sum(o * do).
 
     ``o`` and ``lse`` are what fa_fwd returned for (q, k, v).  ``workspace`` (a uint8 device
     tensor of at least fa_bwd_workspace_size bytes) may be passed to avoid an allocation.
+    ``events``: optional list of FA_BWD_LAUNCHES + 1 torch.cuda.Event(enable_timing=True);
+    the library records events[i] before its launch i and the last one after (fa_bwd_timed),
+    so events[i].elapsed_time(events[i + 1]) is the duration of launch i.
     """
     import torch
     lib = load_library()
@@ -153,10 +160,23 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=Fa
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0, code,
-                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                    _stream_handle(stream, dev))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0, code,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    if events is None:
+        st = lib.fa_bwd(*args)
+        where = "fa_bwd"
+    else:
+        if len(events) != FA_BWD_LAUNCHES + 1:
+            raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        handles = (ctypes.c_void_p * len(events))()
+        for n, ev in enumerate(events):
+            if ev.cuda_event == 0:  # torch creates the underlying event on its first record
+                ev.record(s)
+            handles[n] = ev.cuda_event
+        st = lib.fa_bwd_timed(*args, handles)
+        where = "fa_bwd_timed"
     if st != FA_OK:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, where)
     return dq, dk, dv

@@ -49,9 +49,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
     return round_up((size_t)B * H * N * sizeof(float), 256);
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
-           void* workspace, size_t workspace_bytes, void* stream) {
+static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                      int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* events) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
     const int st = check_common(B, H, N, d, scale, dtype);
     if (st != FA_OK) return st;
@@ -61,9 +62,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype) || !aligned(workspace, 256))
         return FA_ERR_WORKSPACE;
     fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0, dtype,
-                  static_cast<float*>(workspace)};
+                  static_cast<float*>(workspace), events};
     const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    if (!events) return FA_ERR_NULL;
+    for (int i = 0; i <= FA_BWD_LAUNCHES; ++i)
+        if (!events[i]) return FA_ERR_NULL;
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
+                      workspace_bytes, stream, events);
 }
 
 const char* fa_status_string(int status) {

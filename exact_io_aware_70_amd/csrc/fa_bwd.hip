@@ -565,37 +565,50 @@ hipError_t launch_delta(const BwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Record the caller's timing event `i` (if any) on the stream.
+hipError_t mark(const BwdArgs& a, int i, hipStream_t st) {
+    return a.events ? hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st) : hipSuccess;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
     constexpr int NW = 4;
-    hipError_t e = launch_delta<__bf16, D>(a, st);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if ((e = mark(a, 0, st)) != hipSuccess) return e;
+    if ((e = launch_delta<__bf16, D>(a, st)) != hipSuccess) return e;
+    if ((e = mark(a, 1, st)) != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)((long long)nkt * a.B * a.H)), dim3(NW * 64), 0,
                        st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
                        (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.N, nkt, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(a, 2, st)) != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)((long long)nqt * a.B * a.H)), dim3(NW * 64), 0, st,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
                        (const float*)a.delta, (__bf16*)a.dq, a.N, nqt, a.scale, a.scale * kLog2e);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(a, 3, st);
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
-    hipError_t e = launch_delta<float, D>(a, st);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if ((e = mark(a, 0, st)) != hipSuccess) return e;
+    if ((e = launch_delta<float, D>(a, st)) != hipSuccess) return e;
+    if ((e = mark(a, 1, st)) != hipSuccess) return e;
     const int nkt = (a.N + 127) / 128;
     hipLaunchKernelGGL((dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)((long long)nkt * a.B * a.H)), dim3(256), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
                        (const float*)a.delta, (float*)a.dk, (float*)a.dv, a.N, nkt, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(a, 2, st)) != hipSuccess) return e;
     const int nqt = (a.N + 127) / 128;
     hipLaunchKernelGGL((dq_f32_kernel<D, CAUSAL>), dim3((unsigned)((long long)nqt * a.B * a.H)), dim3(256), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
                        (const float*)a.delta, (float*)a.dq, a.N, nqt, a.scale, a.scale * kLog2e);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(a, 3, st);
 }
 
 }  // namespace

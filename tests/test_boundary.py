@@ -34,7 +34,8 @@ def test_header_is_plain_c():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version"} <= set(names)
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_status_string",
+            "fa_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -112,6 +113,24 @@ def test_bwd_workspace():
 @pytest.mark.parametrize("kw,code", [(dict(N=0), -2), (dict(d=80), -3), (dict(dtype=5), -3), (dict(scale=0.0), -3)])
 def test_bwd_bad_sizes(kw, code):
     assert call_bwd(**kw) == code
+
+
+def call_bwd_timed(events, **kw):
+    a = dict(GOOD, **kw)
+    return fa.load_library().fa_bwd_timed(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                          a["causal"], a["dtype"], P, 1 << 30, None, events)
+
+
+def test_bwd_timed_rejects_missing_events():
+    """fa_bwd_timed needs FA_BWD_LAUNCHES + 1 event handles; NULL array or handle -> FA_ERR_NULL."""
+    assert fa.FA_BWD_LAUNCHES == 3
+    assert call_bwd_timed(None) == -1
+    handles = (ctypes.c_void_p * (fa.FA_BWD_LAUNCHES + 1))(*([P] * fa.FA_BWD_LAUNCHES + [None]))
+    assert call_bwd_timed(handles) == -1
+    # With all handles present the ordinary checks still run first (nothing is launched).
+    handles = (ctypes.c_void_p * (fa.FA_BWD_LAUNCHES + 1))(*([P] * (fa.FA_BWD_LAUNCHES + 1)))
+    assert call_bwd_timed(handles, d=80) == -3
+    assert call_bwd_timed(handles, N=0) == -2
 
 
 def test_bwd_misaligned():

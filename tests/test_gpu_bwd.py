@@ -81,3 +81,20 @@ def test_bwd_deterministic():
     a = run_bwd(case, True)
     b = run_bwd(case, True)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_bwd_timed_matches_untimed():
+    """fa_bwd_timed does the same work as fa_bwd (bitwise) and its events bracket each launch."""
+    import torch
+    import exact_io_aware_70_amd as fa
+    case = fa_inputs.make_case(1, 2, 500, 64, "bf16", seed=304, with_grad=True)
+    q, k, v, do = (to_device(case, n) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    ref = fa.fa_bwd(q, k, v, o, lse, do, causal=True)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(fa.FA_BWD_LAUNCHES + 1)]
+    got = fa.fa_bwd(q, k, v, o, lse, do, causal=True, events=events)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(ref, got))
+    times = [events[i].elapsed_time(events[i + 1]) for i in range(fa.FA_BWD_LAUNCHES)]
+    log(f"  launch times (ms): {times}")
+    assert all(t > 0 for t in times)
