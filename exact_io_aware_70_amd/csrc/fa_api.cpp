@@ -45,8 +45,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
     if (check_common(B, H, N, d, 1.0f, dtype) != FA_OK) return 0;
-    // D_i = rowsum(dout * o): one float per (batch, head, row).
-    return round_up((size_t)B * H * N * sizeof(float), 256);
+    // D_i = rowsum(dout * o) and lse * log2(e): one float each per (batch, head, row).
+    return 2 * round_up((size_t)B * H * N * sizeof(float), 256);
 }
 
 static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -61,8 +61,9 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
         return FA_ERR_ALIGN;
     if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype) || !aligned(workspace, 256))
         return FA_ERR_WORKSPACE;
-    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0, dtype,
-                  static_cast<float*>(workspace), events};
+    float* delta = static_cast<float*>(workspace);
+    float* lse2 = delta + round_up((size_t)B * H * N * sizeof(float), 256) / sizeof(float);
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal ? 1 : 0, dtype, delta, lse2, events};
     const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -11,7 +11,7 @@
 //     dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on one stream, no atomics (run-to-run bitwise deterministic):
-//   1. delta:  D_i = rowsum(dO * O) into the caller's workspace;
+//   1. delta:  D_i = rowsum(dO * O) and lse * log2(e) into the caller's workspace;
 //   2. dK/dV:  one workgroup per key tile, each wave holding 32 keys (K, V fragments and
 //              the dK^T, dV^T accumulators in registers), walking the query tiles;
 //   3. dQ:     one workgroup per query tile, each wave holding 32 queries, walking the key
@@ -26,9 +26,12 @@ namespace fa {
 namespace {
 
 // ------------------------------------------------------------------ delta = rowsum(dO * O)
+// Also writes lse2 = lse * log2(e), the form in which the recomputing kernels use lse
+// (P = 2^(scale log2(e) s - lse2)), so they need no per-score conversion.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                     float* __restrict__ Delta, long long rows) {
+                                                     const float* __restrict__ LSE, float* __restrict__ Delta,
+                                                     float* __restrict__ LSE2, long long rows) {
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;         // chunks (threads) per row
     constexpr int RPB = 256 / CPR;       // rows per block
@@ -51,7 +54,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
     }
 #pragma unroll
     for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && c == 0) Delta[row] = acc;
+    if (row < rows && c == 0) {
+        Delta[row] = acc;
+        LSE2[row] = LSE[row] * kLog2e;
+    }
 }
 
 // ------------------------------------------------------------------ bf16 dK / dV
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
 template <int D, int NW, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2) {
     constexpr int BQ = 32;              // query rows per sub-tile
     constexpr int NS = 4;               // LDS stages
@@ -84,7 +90,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     __shared__ __attribute__((aligned(1024))) __bf16 dOs[NS][STAGE];
     // lse and D rows of each stage; each 64-lane 4-byte load fills one 64-float row (lanes
     // past the sub-tile read zeros into the unused upper half).
-    __shared__ __attribute__((aligned(256))) float LDs[NS][2][64];
+    __shared__ __attribute__((aligned(256))) float LDs[NS][2][64];  // lse2 | D
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
@@ -136,7 +142,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             load_lds_b128(rq, lds_addr(&Qs[ST][(j * NT + wave * 64) * 8]), voff[j]);
             load_lds_b128(ro, lds_addr(&dOs[ST][(j * NT + wave * 64) * 8]), voff[j]);
         }
-        const i32x4 rl = make_rsrc(LSE + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
+        const i32x4 rl = make_rsrc(LSE2 + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
         const i32x4 rd = make_rsrc(Delta + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
         load_lds_b32(rl, lds_addr(&LDs[ST][0][0]), (uint32_t)(lane * 4));
         load_lds_b32(rd, lds_addr(&LDs[ST][1][0]), (uint32_t)(lane * 4));
@@ -170,17 +176,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             sacc = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE), kf[kc], sacc);
             pacc = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE + DO_OFF), vf[kc], pacc);
         }
-        const bool diag = CAUSAL && t == wave_first;
+        // Causal: on the wave's diagonal sub-tile, key mykey > query t*BQ + 8(r/4) + 4 half + r%4
+        // is masked, i.e. thr > 8(r/4) + r%4 with thr = l32 - 4 half; elsewhere thr = -1.
+        const int thr = (CAUSAL && t == wave_first) ? (l32 - 4 * half) : -1;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&LDs[ST][0][8 * g + 4 * half]);
-            const f32x4 del4 = *reinterpret_cast<const f32x4*>(&LDs[ST][1][8 * g + 4 * half]);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&LDs[ST][0][8 * g + 4 * half]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&LDs[ST][1][8 * g + 4 * half]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -lse4[e] * kLog2e));
-                if (diag && mykey > t * BQ + 8 * g + 4 * half + e) p = 0.f;
+                float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -l4[e]));
+                if (CAUSAL && thr > 8 * g + e) p = 0.f;
                 sacc[4 * g + e] = p;
-                pacc[4 * g + e] = p * (pacc[4 * g + e] - del4[e]);
+                pacc[4 * g + e] = p * (pacc[4 * g + e] - d4[e]);
             }
         }
         const bf16x8 pb[2] = {to_bf16x8(sacc, 0), to_bf16x8(sacc, 8)};
@@ -249,7 +257,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 template <int D, int NW, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2) {
     constexpr int BK = 32, NS = 4, STAGE = BK * D, CPR = D / 8, NT = NW * 64;
     constexpr int BM = 32 * NW, DC = D / 16, DB = D / 32;
@@ -279,7 +287,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         }
     }
     // Rows past N: lse = +inf makes their P exactly 0 (they are not stored either).
-    const float lse2 = (myq < N) ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
+    const float lse2 = (myq < N) ? LSE2[(size_t)bh * N + myq] : INFINITY;
     const float del = (myq < N) ? Delta[(size_t)bh * N + myq] : 0.f;
     wait_vmcnt<0>();
 
@@ -336,16 +344,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             s = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE), qf[kc], s);
             dp = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE + V_OFF), of[kc], dp);
         }
-        const bool need_mask = CAUSAL ? (kv0 + BK - 1 > wq0) : (kv0 + BK > N);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-            if (need_mask) {
+        for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+        if (CAUSAL ? (kv0 + BK - 1 > wq0) : (kv0 + BK > N)) {  // diagonal or tail sub-tile
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
                 const int key = kv0 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (CAUSAL ? (key > myq) : (key >= N)) p = 0.f;
+                if (CAUSAL ? (key > myq) : (key >= N)) s[r] = 0.f;
             }
-            dp[r] = p * (dp[r] - del);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
         const bf16x8 sb[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
@@ -561,7 +570,7 @@ hipError_t launch_delta(const BwdArgs& a, hipStream_t st) {
     const long long rows = (long long)a.B * a.H * a.N;
     const long long grid = (rows + RPB - 1) / RPB;
     hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)a.o, (const T*)a.dout,
-                       a.delta, rows);
+                       a.lse, a.delta, a.lse2, rows);
     return hipGetLastError();
 }
 
@@ -579,14 +588,15 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
     if ((e = mark(a, 1, st)) != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)((long long)nkt * a.B * a.H)), dim3(NW * 64), 0,
-                       st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.N, nkt, a.scale, a.scale * kLog2e);
+                       st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
+                       (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.N, nkt, a.scale,
+                       a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(a, 2, st)) != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)((long long)nqt * a.B * a.H)), dim3(NW * 64), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       (const float*)a.delta, (__bf16*)a.dq, a.N, nqt, a.scale, a.scale * kLog2e);
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
+                       (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dq, a.N, nqt, a.scale, a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(a, 3, st);
 }

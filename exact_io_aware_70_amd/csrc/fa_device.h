@@ -71,6 +71,35 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Value held by lane (l ^ 32): the other half of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// v_permlane32_swap on (x, x) leaves the lower-half values in every lane of the first
+// result and the upper-half values in every lane of the second, so max / sum of the pair is
+// the combination over lanes l and l ^ 32, in all 64 lanes, with one cross-lane instruction.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum of the 16 values of an accumulator tile (a max3 tree: 8 VALU operations).
+__device__ __forceinline__ float max16(const f32x16& a) {
+    const float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]), m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+    const float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]), m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+    const float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+    return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), a[15]));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// acc + sum of the eight bf16 values of v (four v_dot2 against (1, 1), fp32 accumulation).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+    return acc;
+}
+
 // Buffer resource (raw, stride 0) over `bytes` bytes starting at `base`, as four SGPRs.
 // Loads through it return 0 for any byte offset at or past `bytes`, so ragged tails need no
 // address clamping.  `base` and `bytes` must be uniform across the wave.

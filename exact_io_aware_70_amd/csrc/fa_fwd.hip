@@ -185,11 +185,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         bool up = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float mx = fmaxf(s[qb][0], s[qb][1]);
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
-            mx = fmaxf(mx, swap_halves(mx));
-            mt[qb] = mx * scale_log2;
+            mt[qb] = max_halves(max16(s[qb])) * scale_log2;
             up |= mt[qb] > m_ref[qb] + kRescaleSlack;
         }
         if (__any(up)) {
@@ -214,17 +210,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             pb[qb][1] = to_bf16x8(s[qb], 8);
         }
     };
-    auto rowsum = [&](const f32x16 (&p)[QB]) {
+    // Row sums of the bf16-rounded P(t) (the values the P V product uses), two per v_dot2.
+    auto rowsum = [&](const bf16x8 (&pb)[QB][2]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float a = 0.f, b = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                a += p[qb][r];
-                b += p[qb][r + 1];
-            }
-            lsum[qb] += a + b;
-        }
+        for (int qb = 0; qb < QB; ++qb) lsum[qb] = sum_bf16x8(pb[qb][1], sum_bf16x8(pb[qb][0], lsum[qb]));
     };
     // O^T += V^T P^T for the sub-tile in stage ST: for k-step cc the B operand holds keys
     // 16cc + 8(i/4) + 4 half + i%4, and the two transposed reads fetch V^T at exactly those
@@ -284,7 +273,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         pin_regs(pb);  // keep the exponentials in region 1 (they would sink to their use)
         if (needs_mask(i + 1)) mask(i + 1, nxt);
         pv(cur_st, pb);
-        rowsum(cur);
+        rowsum(pb);
         raise_ref(nxt);
     };
     int i = 0;
@@ -301,7 +290,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     // Epilogue: O = acc / l, lse = m_ref ln 2 + ln l.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float l = lsum[qb] + swap_halves(lsum[qb]);
+        const float l = sum_halves(lsum[qb]);
         const int myq = wq0 + 32 * qb + l32;
         if (myq < N) {
             const float inv = 1.0f / l;

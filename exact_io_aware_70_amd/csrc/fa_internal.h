@@ -36,6 +36,7 @@ struct BwdArgs {
     int causal;
     int dtype;
     float* delta;  // workspace: D_i = rowsum(dout * o), float [B, H, N]
+    float* lse2;   // workspace: lse * log2(e), float [B, H, N]
     void* const* events;  // optional: hipEvent_t recorded before each launch and after the last
 };
 
