@@ -162,31 +162,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     }
     constexpr int DO_OFF = (int)(sizeof(Qs) / sizeof(__bf16));  // dOs follows Qs in the same layout
 
-    auto step = [&](auto st, int i) {
-        constexpr int ST = decltype(st)::value;
-        wait_vmcnt<(NS - 2) * LPS>();  // sub-tile i has landed (this wave's share) ...
-        __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
-        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, t_begin + i + NS - 1);
-        const int t = t_begin + i;
-        if (!wave_live || t < wave_first) return;
+    // The arithmetic of one query sub-tile whose rows start at stage offset `so` (elements);
+    // MASKED applies the causal mask of the wave's own diagonal sub-tile (query rows
+    // kw0 .. kw0 + 31: key l32 > query 8(r/4) + 4 half + r%4).
+    auto body = [&](auto masked, int so, int ls) {
+        constexpr bool MASKED = decltype(masked)::value;
         // S = Q K^T and dP = dO V^T: lane = key, register r = query 8(r/4) + 4 half + r%4.
         f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < DC; ++kc) {
-            sacc = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE), kf[kc], sacc);
-            pacc = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE + DO_OFF), vf[kc], pacc);
+            sacc = mfma_bf16(load_bf16x8(r_lane[kc] + so), kf[kc], sacc);
+            pacc = mfma_bf16(load_bf16x8(r_lane[kc] + so + DO_OFF), vf[kc], pacc);
         }
-        // Causal: on the wave's diagonal sub-tile, key mykey > query t*BQ + 8(r/4) + 4 half + r%4
-        // is masked, i.e. thr > 8(r/4) + r%4 with thr = l32 - 4 half; elsewhere thr = -1.
-        const int thr = (CAUSAL && t == wave_first) ? (l32 - 4 * half) : -1;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&LDs[ST][0][8 * g + 4 * half]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&LDs[ST][1][8 * g + 4 * half]);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&LDs[ls][0][8 * g + 4 * half]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&LDs[ls][1][8 * g + 4 * half]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -l4[e]));
-                if (CAUSAL && thr > 8 * g + e) p = 0.f;
+                if (MASKED && l32 > 8 * g + 4 * half + e) p = 0.f;
                 sacc[4 * g + e] = p;
                 pacc[4 * g + e] = p * (pacc[4 * g + e] - d4[e]);
             }
@@ -199,13 +194,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int off = ST * STAGE + 16 * cc * D;
+                const int off = so + 16 * cc * D;
                 const bf16x8 a_do = join_tr(lds_read_tr16(t_lane[0][db] + off + DO_OFF),
                                             lds_read_tr16(t_lane[1][db] + off + DO_OFF));
                 dv[db] = mfma_bf16(a_do, pb[cc], dv[db]);
                 const bf16x8 a_q = join_tr(lds_read_tr16(t_lane[0][db] + off), lds_read_tr16(t_lane[1][db] + off));
                 dk[db] = mfma_bf16(a_q, sb[cc], dk[db]);
             }
+    };
+
+    // Causal: the ring pass covers the sub-tiles strictly after each wave's diagonal one, so
+    // its body needs no mask; the diagonal sub-tile is done once at the end (below).
+    auto step = [&](auto st, int i) {
+        constexpr int ST = decltype(st)::value;
+        wait_vmcnt<(NS - 2) * LPS>();  // sub-tile i has landed (this wave's share) ...
+        __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
+        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, t_begin + i + NS - 1);
+        const int t = t_begin + i;
+        if (!wave_live || (CAUSAL ? t <= wave_first : false)) return;
+        body(std::false_type{}, ST * STAGE, ST);
     };
 
     using S0 = std::integral_constant<int, 0>;
@@ -226,7 +233,33 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     if (i < nsteps) step(S0{}, i);
     if (i + 1 < nsteps) step(S1{}, i + 1);
     if (i + 2 < nsteps) step(S2{}, i + 2);
-    wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the wave ends
+    wait_vmcnt<0>();  // the ring's loads have landed ...
+
+    if constexpr (CAUSAL) {
+        static_assert(NS >= NW, "each wave needs a stage of its own for its diagonal sub-tile");
+        __syncthreads();  // ... and every wave is done reading the ring
+        if (wave_live) {
+            // The diagonal sub-tile (query rows kw0 .. kw0 + 31) into this wave's own stage;
+            // only this wave reads it, so its own vmcnt wait is enough.
+            const int q0 = kw0;
+            const uint32_t rows = (uint32_t)max(0, N - q0);
+            const i32x4 rq = make_rsrc(Q + base + (size_t)q0 * D, rows * D * 2);
+            const i32x4 ro = make_rsrc(dO + base + (size_t)q0 * D, rows * D * 2);
+#pragma unroll
+            for (int j = 0; j < BQ * CPR / 64; ++j) {
+                const int g = j * 64 + lane, r = g / CPR, c = (g % CPR) ^ swz_row<D>(r);
+                const uint32_t vo = (uint32_t)((r * D + c * 8) * 2);
+                load_lds_b128(rq, lds_addr(&Qs[wave][j * 64 * 8]), vo);
+                load_lds_b128(ro, lds_addr(&dOs[wave][j * 64 * 8]), vo);
+            }
+            const i32x4 rl = make_rsrc(LSE2 + rbase + q0, min(rows, (uint32_t)BQ) * 4);
+            const i32x4 rd = make_rsrc(Delta + rbase + q0, min(rows, (uint32_t)BQ) * 4);
+            load_lds_b32(rl, lds_addr(&LDs[wave][0][0]), (uint32_t)(lane * 4));
+            load_lds_b32(rd, lds_addr(&LDs[wave][1][0]), (uint32_t)(lane * 4));
+            wait_vmcnt<0>();
+            body(std::true_type{}, wave * STAGE, wave);
+        }
+    }
 
     if (mykey < N) {
         __bf16* dkrow = dK + base + (size_t)mykey * D;
