@@ -286,6 +286,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     if (i < nt) step(S0{}, i, sa, sb);
     if (i + 1 < nt) step(S1{}, i + 1, sb, sa);
     if (i + 2 < nt) step(S2{}, i + 2, sa, sb);
+    wait_vmcnt<0>();  // no LDS-direct load may still be writing when the workgroup's LDS is freed
 
     // Epilogue: O = acc / l, lse = m_ref ln 2 + ln l.
 #pragma unroll
