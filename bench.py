@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--copy-mib M] [--workload NAME]
+    python bench.py --summarize-sq STATS_CSV PMC_DIR [PMC_DIR ...] [--workload NAME]
 
 One step = the whole hot path over one batch: fa_fwd (tiled online-softmax forward,
 writing O and lse) followed by fa_bwd (D = rowsum(dO * O), dK/dV and dQ by recomputation)
@@ -56,6 +57,10 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, both with "
                         "--copy-mib) into profiles/hbm_traffic_<workload>.txt, then exit")
+    p.add_argument("--summarize-sq", nargs="+", metavar="PATH",
+                   help="a rocprofv3 kernel_stats.csv followed by the output folders of rocprofv3 --pmc runs "
+                        "of this script with SQ_* / GRBM_GUI_ACTIVE counters: write "
+                        "profiles/mfma_util_<workload>.md (MFMA, VALU and LDS use per kernel), then exit")
     return p.parse_args()
 
 
@@ -81,8 +86,8 @@ def kernel_table(dtype, B, H, N, d, causal):
     return {
         # two products (S = Q K^T, O = P V), 2 N^2 d flops each per head
         f"fwd_{sfx}_kernel": ("mfma", 4.0 * n2d, "flop"),
-        # reads O and dO once, writes one float per row
-        "delta_kernel": ("hbm", 2.0 * B * H * N * d * elt + 4.0 * B * H * N, "byte"),
+        # reads O, dO and lse once; writes D and lse * log2(e), one float each per row
+        "delta_kernel": ("hbm", 2.0 * B * H * N * d * elt + 12.0 * B * H * N, "byte"),
         # four products: S, dP, dV += P^T dO, dK += dS^T Q
         f"dkdv_{sfx}_kernel": ("mfma", 8.0 * n2d, "flop"),
         # three products: S and dP (recomputed) and dQ += dS K
@@ -158,6 +163,85 @@ def summarize_pmc(args):
     print(json.dumps(data, indent=1))
 
 
+def read_counters(dirs):
+    """Mean per dispatch of every counter, per kernel (short name), over rocprofv3 --pmc folders."""
+    names = ["fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel"]
+    per = {}  # (short, counter) -> {dispatch: value}
+    for d in dirs:
+        for dp, _, files in os.walk(d):
+            for fn in files:
+                if not fn.endswith("counter_collection.csv"):
+                    continue
+                with open(os.path.join(dp, fn)) as f:
+                    for r in csv.DictReader(f):
+                        short = next((n for n in names if n in r["Kernel_Name"]), None)
+                        if short is None:
+                            continue
+                        slot = per.setdefault((short, r["Counter_Name"]), {})
+                        key = (d, r["Dispatch_Id"])
+                        slot[key] = slot.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (short, counter), vals in per.items():
+        out.setdefault(short, {})[counter] = sum(vals.values()) / len(vals)
+    return out
+
+
+def summarize_sq(args):
+    """MFMA, VALU and LDS use per kernel from SQ counters, as a short markdown table.
+
+    The chip has 256 CUs of 4 SIMDs in 8 XCDs; GRBM_GUI_ACTIVE is summed over the XCDs, so
+    one XCD's busy cycles are an eighth of it, and the clock is those cycles over the kernel's
+    average duration (from the kernel-trace statistics given first).  A 32x32x16 bf16 MFMA
+    keeps its SIMD's matrix core busy for 32 cycles (SQ_VALU_MFMA_BUSY_CYCLES counts exactly
+    that), so MFMA busy = busy cycles / (1024 SIMDs x cycles)."""
+    stats_csv, dirs = args.summarize_sq[0], args.summarize_sq[1:]
+    dur = {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            for n in ("fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel"):
+                if n in r["Name"]:
+                    dur[n] = float(r["AverageNs"]) * 1e-9
+    c = read_counters(dirs)
+    import fa_inputs
+    w = fa_inputs.CONFIGS[args.workload]
+    table = kernel_table(w["dtype"], w["B"], w["H"], w["N"], w["d"], w["causal"])
+    lines = [f"# MFMA, VALU and LDS use per kernel: {args.workload}", "",
+             "Commands (from the repository root, on one MI355X; one `--pmc` run per counter group):", ""]
+    for d in dirs:
+        lines.append(f"    rocprofv3 --pmc <counters of {os.path.basename(d.rstrip('/'))}> -d {d} -- "
+                     f"python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --workload {args.workload}")
+    lines += [f"    python3 bench.py --summarize-sq {stats_csv} {' '.join(dirs)} --workload {args.workload}", "",
+              "Counter values are means per dispatch (one warm-up and one timed step).  Durations come from "
+              "the kernel-trace statistics named above.", "",
+              "| kernel | ms | clock (GHz) | MFMA instr. / algorithmic | MFMA busy | MFMA busy with VALU co-issue "
+              "| other VALU instr. per MFMA (exp included) | exp per MFMA | LDS instr. per MFMA | CU busy |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for n in ("fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel"):
+        k = c.get(n, {})
+        if "GRBM_GUI_ACTIVE" not in k or n not in dur:
+            continue
+        cyc = k["GRBM_GUI_ACTIVE"] / 8.0
+        clock = cyc / dur[n] / 1e9
+        mfma = k.get("SQ_INSTS_MFMA", float("nan"))
+        algo = table[n][1] / 32768.0
+        busy = k.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (1024.0 * cyc)
+        coex = k.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")) / k.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+        valu = (k.get("SQ_INSTS_VALU", float("nan")) - mfma) / mfma
+        trans = k.get("SQ_INSTS_VALU_TRANS_F32", float("nan")) / mfma
+        lds = k.get("SQ_INSTS_LDS", float("nan")) / mfma
+        cu = k.get("SQ_BUSY_CU_CYCLES", float("nan")) / (256.0 * cyc)
+        lines.append(f"| {n} | {dur[n] * 1e3:.3f} | {clock:.2f} | {mfma / algo:.3f} | {busy:.1%} | {coex:.1%} "
+                     f"| {valu:.2f} | {trans:.2f} | {lds:.2f} | {cu:.1%} |")
+    lines += ["", "Raw means per dispatch:", "", "| kernel | counter | value |", "|---|---|---|"]
+    for n in sorted(c):
+        for counter in sorted(c[n]):
+            lines.append(f"| {n} | {counter} | {c[n][counter]:.4g} |")
+    path = os.path.join(ROOT, "profiles", f"mfma_util_{args.workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(case, causal, heads):
     """The fp64 oracle (as it stands) on `heads` heads of the workload: forward + backward."""
     import numpy as np
@@ -190,6 +274,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_sq:
+        summarize_sq(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
