@@ -15,6 +15,13 @@ FlashAttention in PyTorch", which draws q, k, v with randn):
   fwd_bf16_causal_b1h32_n16384_d128 fwd   bf16   1  32  16384  128  yes     4  (rows seed 1004)
   bwd_bf16_causal_b4h16_n4096_d128  bwd   bf16   4  16  4096   128  yes     5
 
+Row-softmax workloads (the softmax step of attention on its own: logits of unit
+Gaussian q and k scaled by 1/sqrt(d) are N(0, 1)):
+
+  name                          dtype  rows    cols  seed
+  softmax_bf16_r65536_c8192     bf16   65536   8192  11   (8 heads' score rows at N = 8192)
+  softmax_f32_r8192_c2048       f32    8192    2048  12
+
 Recipe: ``np.random.default_rng(seed).standard_normal(shape, dtype=float32)`` drawn
 in the order Q, K, V (then dO for backward cases); Q multiplied by ``q_scale`` in
 fp32; then rounded to the storage dtype (bf16 with round-to-nearest-even).  The
@@ -38,6 +45,11 @@ CONFIGS = {
                                               row_seed=1004, rows_per_head=256),
     "bwd_bf16_causal_b4h16_n4096_d128": dict(pass_="bwd", dtype="bf16", B=4, H=16, N=4096,
                                              d=128, causal=True, seed=5, q_scale=1.0),
+}
+
+SOFTMAX_CONFIGS = {
+    "softmax_bf16_r65536_c8192": dict(dtype="bf16", rows=65536, cols=8192, seed=11, x_scale=1.0),
+    "softmax_f32_r8192_c2048": dict(dtype="f32", rows=8192, cols=2048, seed=12, x_scale=1.0),
 }
 
 
@@ -105,3 +117,30 @@ def sample_rows(B: int, H: int, N: int, rows_per_head: int, seed: int) -> np.nda
         for h in range(H):
             out[b, h] = np.sort(rng.choice(N, size=r, replace=False))
     return out
+
+
+def make_softmax_case(rows: int, cols: int, dtype: str, seed: int, x_scale: float = 1.0,
+                      mask: str | None = None) -> dict:
+    """Logits of one row-softmax case, as stored values.
+
+    ``x_scale`` multiplies the N(0, 1) draw (float32) before rounding to the storage
+    dtype.  ``mask="causal"`` sets entry (r, c) to -inf for c > r mod cols (the visible
+    keys of a causal score row); ``mask="empty-rows"`` also makes every 7th row all -inf.
+    Returns ``{"dtype", "shape", "bits" or None, "values": float32 [rows, cols]}``.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    x = np.random.default_rng(seed).standard_normal((rows, cols), dtype=np.float32)
+    if x_scale != 1.0:
+        x *= np.float32(x_scale)
+    if mask in ("causal", "empty-rows"):
+        r = np.arange(rows)[:, None] % cols
+        x[np.arange(cols)[None, :] > r] = -np.inf
+        if mask == "empty-rows":
+            x[::7] = -np.inf
+    elif mask is not None:
+        raise ValueError(f"unknown mask {mask!r}")
+    if dtype == "bf16":
+        bits = bf16_bits(x)
+        return {"dtype": dtype, "shape": (rows, cols), "bits": bits, "values": bf16_bits_to_f32(bits)}
+    return {"dtype": dtype, "shape": (rows, cols), "bits": None, "values": x}

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for exact attention -- test infrastructure only.
+"""fp64 CPU oracle for exact attention and the row-wise softmax -- test infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 leg may import this package.  The HIP library and its Python binding never do,
@@ -10,3 +10,4 @@ inputs, finite differences and a library special case); none is "parity unpinned
 """
 from .attention import backward, forward, forward_rows, probabilities, scores  # noqa: F401
 from .online import chunk_merge, tiled_forward  # noqa: F401
+from .softmax import softmax_rows  # noqa: F401

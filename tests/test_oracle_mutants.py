@@ -139,3 +139,45 @@ def test_unmutated_copies_pass():
         pin(fwd) if pin is not pins.pin_two_key_example else pin(fwd, bwd)
     for pin in pins.BACKWARD_PINS:
         pin(fwd, bwd)
+
+
+def _make_softmax(mistake):
+    def fn(x):
+        x = np.asarray(x, dtype=np.float64)
+        with np.errstate(all="ignore"):
+            m = np.zeros(x.shape[0]) if mistake == "max not subtracted" else np.max(x, axis=1)
+            if mistake == "max over columns":
+                m = np.broadcast_to(np.max(x), x.shape[:1])
+            e = np.exp(x - m[:, None])
+            l = np.sum(e, axis=1)
+            if mistake == "normalised over the whole array":
+                l = np.full(x.shape[0], np.sum(e))
+            y = e / l[:, None]
+            lse = (0.0 if mistake == "lse without the max" else m) + (
+                np.log10(l) if mistake == "lse in log10" else np.log(l))
+        return y, lse
+    return fn
+
+
+SOFTMAX_MUTANTS = ["max not subtracted", "max over columns", "normalised over the whole array", "lse without the max",
+                   "lse in log10"]
+
+
+@pytest.mark.parametrize("name", SOFTMAX_MUTANTS)
+def test_softmax_mutant_is_caught(name):
+    from tests import softmax_pins
+    fn = _make_softmax(name)
+    failures = 0
+    for pin in softmax_pins.SOFTMAX_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no softmax pin caught the planted mistake: {name}"
+
+
+def test_unmutated_softmax_copy_passes():
+    from tests import softmax_pins
+    fn = _make_softmax(None)
+    for pin in softmax_pins.SOFTMAX_PINS:
+        pin(fn)
