@@ -1,6 +1,7 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --workload softmax_bf16_r65536_c8192   (the row-softmax kernel on its own)
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--copy-mib M] [--workload NAME]
     python bench.py --summarize-sq STATS_CSV PMC_DIR [PMC_DIR ...] [--workload NAME]
 
@@ -41,6 +42,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 KERNEL_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd.hip", "exact_io_aware_70_amd/csrc/fa_bwd.hip",
                   "exact_io_aware_70_amd/csrc/fa_device.h"]
+SOFTMAX_SOURCES = ["exact_io_aware_70_amd/csrc/fa_softmax.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
 
 
 def parse():
@@ -51,6 +53,8 @@ def parse():
     p.add_argument("--workload", default="fwd_bf16_causal_b4h32_n8192_d128")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=16, help="heads of the workload the CPU oracle runs")
+    p.add_argument("--cpu-rows", type=int, default=65536,
+                   help="rows of a row-softmax workload the CPU oracle runs")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="before the steps, copy this many MiB once with a plain device copy: the reference "
                         "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM byte counts")
@@ -69,9 +73,14 @@ def flops(B, H, N, d, causal):
     return 4.0 * B * H * N * N * d * f, 10.0 * B * H * N * N * d * f
 
 
-def sources_digest() -> str:
+def is_softmax(workload) -> bool:
+    return workload.startswith("softmax_")
+
+
+def sources_digest(workload="") -> str:
+    """SHA-256 of the kernel sources a workload runs (the counter summaries record it)."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in (SOFTMAX_SOURCES if is_softmax(workload) else KERNEL_SOURCES):
         with open(os.path.join(ROOT, path), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -106,7 +115,7 @@ def load_traffic(workload):
         return None
     with open(path) as f:
         data = json.load(f)
-    if data.get("source_sha256") != sources_digest():
+    if data.get("source_sha256") != sources_digest(workload):
         return None  # the kernels changed since the counters were taken
     return data["kernels"]
 
@@ -137,7 +146,7 @@ def summarize_pmc(args):
 
     ff, fw = calib(fetch), calib(write)
     names = ["fwd_bf16_kernel", "fwd_f32_kernel", "delta_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
-             "dq_bf16_kernel", "dq_f32_kernel"]
+             "dq_bf16_kernel", "dq_f32_kernel", "softmax_rows_kernel"]
     out = {}
     for short in names:
         fv = [v for (_, n), v in fetch.items() if short in n]
@@ -147,7 +156,7 @@ def summarize_pmc(args):
             wb = sum(wv) / len(wv) * 1024.0 * fw
             out[short] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes": round(fb + wb),
                           "dispatches": len(fv)}
-    data = {"workload": args.workload, "source_sha256": sources_digest(),
+    data = {"workload": args.workload, "source_sha256": sources_digest(args.workload),
             "fetch_scale": ff, "write_scale": fw, "copy_mib": args.copy_mib,
             "commands": [f"rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -- python3 bench.py --steps 1 --warmup 1 "
                          f"--no-cpu-baseline --copy-mib {args.copy_mib} --workload {args.workload}",
@@ -270,6 +279,105 @@ def cpu_baseline(case, causal, heads):
             "seconds": round(t_total, 3)}
 
 
+def softmax_bytes(rows, cols, dtype):
+    """Algorithmic HBM bytes of one row-softmax launch: x read once, y and lse written once."""
+    return 2.0 * rows * cols * (2 if dtype == "bf16" else 4) + 4.0 * rows
+
+
+def cpu_softmax_baseline(case, rows):
+    """The fp64 oracle (as it stands) on the first `rows` rows of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    R, C = case["shape"]
+    rows = min(rows, R)
+    x = case["values"][:rows]
+    t0 = time.perf_counter()
+    oracle.softmax_rows(x)
+    t = time.perf_counter() - t0
+    return {"value": round(softmax_bytes(rows, C, case["dtype"]) / t / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"{rows} of {R} rows, cols={C}: fp64 softmax and logsumexp ({t:.1f} s); "
+                                        f"same byte formula as value", "seconds": round(t, 3)}
+
+
+def bench_softmax(args):
+    """One step = one fa_softmax_rows launch over the whole [rows, cols] array."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_70_amd as fa
+    import fa_inputs
+
+    c = fa_inputs.SOFTMAX_CONFIGS[args.workload]
+    case = fa_inputs.make_softmax_case(c["rows"], c["cols"], c["dtype"], c["seed"], c["x_scale"])
+    dev = torch.device("cuda:0")
+    if case["dtype"] == "bf16":
+        x = torch.from_numpy(case["bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(case["values"]).to(dev)
+    y = torch.empty_like(x)
+    lse = torch.empty((c["rows"],), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib * (1 << 20), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        fa.fa_softmax_rows(x, y, lse, stream=stream)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in events:
+        ev[0].record(stream)
+        fa.fa_softmax_rows(x, y, lse, stream=stream)
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[0].elapsed_time(ev[1]) for ev in events]
+    avg = float(np.mean(ms))
+    nbytes = softmax_bytes(c["rows"], c["cols"], c["dtype"])
+    ms_step = wall * 1e3 / args.steps
+    ach = nbytes / (avg * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    tb = traffic.get("softmax_rows_kernel", {}).get("bytes") if traffic else None
+    out = {
+        "metric": "row softmax + logsumexp GB/s (algorithmic bytes: x read once, y and lse written once)",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c["dtype"],
+        "data": "synthetic (seeded N(0,1) logits)",
+        "config": {"workload": args.workload, "rows": c["rows"], "cols": c["cols"], "bytes_per_step": nbytes},
+        "kernels": {"softmax_rows_kernel": {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "bound": "hbm",
+                                            "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                            "frac": round(ach / PEAK_HBM_GBS, 4), "units_per_launch": nbytes,
+                                            "traffic": tb}},
+        "roofline": {"kernel": "softmax_rows_kernel", "bound": "hbm", "achieved": round(ach, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": tb,
+                     "launch_ms": round(avg, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_softmax_baseline(case, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -282,6 +390,10 @@ def main():
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(heads shard across GPUs with no exchange, so one GPU runs one share).", file=sys.stderr)
         sys.exit(2)
+
+    if is_softmax(args.workload):
+        bench_softmax(args)
+        return
 
     import numpy as np
     import torch

@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp,
                                  ctypes.POINTER(vp)]
     lib.fa_bwd_timed.restype = i
+    lib.fa_softmax_rows.argtypes = [vp, vp, vp, ctypes.c_longlong, i, i, vp]
+    lib.fa_softmax_rows.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -180,3 +182,30 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=Fa
     if st != FA_OK:
         raise FAError(st, where)
     return dq, dk, dv
+
+
+def fa_softmax_rows(x, y=None, lse=None, with_lse=True, stream=None):
+    """Row-wise softmax of a 2-D [rows, cols] tensor: returns (y, lse or None).
+
+    ``y`` (x's shape and dtype; may be ``x`` itself for in place) and ``lse`` ([rows]
+    float32) may be passed preallocated; ``with_lse=False`` skips the logsumexp.  Work is
+    enqueued on ``stream`` (default: the current torch stream) without waiting.
+    """
+    import torch
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    rows, cols = x.shape
+    dev = x.device
+    _check("x", x, (rows, cols), x.dtype, dev)
+    y = torch.empty_like(x) if y is None else y
+    _check("y", y, (rows, cols), x.dtype, dev)
+    if with_lse and lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check("lse", lse, (rows,), torch.float32, dev)
+    st = lib.fa_softmax_rows(x.data_ptr(), y.data_ptr(), None if lse is None else lse.data_ptr(), rows, cols,
+                             _dtype_code(x), _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_softmax_rows")
+    return y, lse

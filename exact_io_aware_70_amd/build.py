@@ -22,11 +22,14 @@ LIB = os.path.join(HERE, "libfa.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_softmax.hip"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
                 "-Wall", "-Wno-unused-function"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
                 "-fno-honor-nans"]
+# Per-file additions (later flags win): the row softmax promises NaN rows for all -inf
+# input rows, so it keeps IEEE NaN semantics.
+FILE_FLAGS = {"fa_softmax.hip": ["-fhonor-nans"]}
 
 
 def hipcc() -> str:
@@ -41,7 +44,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + COMMON_FLAGS
     if src.endswith(".hip"):
-        cmd += ["-x", "hip"] + DEVICE_FLAGS
+        cmd += ["-x", "hip"] + DEVICE_FLAGS + FILE_FLAGS.get(src, [])
     cmd += ["-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

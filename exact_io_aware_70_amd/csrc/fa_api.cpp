@@ -85,11 +85,22 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                       workspace_bytes, stream, events);
 }
 
+int fa_softmax_rows(const void* x, void* y, float* lse, long long rows, int cols, int dtype, void* stream) {
+    if (!x || !y) return FA_ERR_NULL;
+    // One workgroup per row at most: keep the 1-D grid in range.
+    if (rows < 1 || cols < 1 || rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(y, 16) || (lse && !aligned(lse, 4))) return FA_ERR_ALIGN;
+    fa::SoftmaxArgs a{x, y, lse, rows, cols, dtype};
+    const hipError_t e = fa::launch_softmax(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H and N must be >= 1 and the grid must fit in 2^31 - 1 tiles";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be >= 1 and the grid must fit in 2^31 - 1 workgroups";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64 or 128, dtype FA_F32 or FA_BF16, scale finite and > 0";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned (lse 4-byte)";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than fa_bwd_workspace_size()";

@@ -40,9 +40,20 @@ struct BwdArgs {
     void* const* events;  // optional: hipEvent_t recorded before each launch and after the last
 };
 
-// Enqueue the forward / backward kernels on `st`; return hipGetLastError() of the launches.
+struct SoftmaxArgs {
+    const void* x;
+    void* y;
+    float* lse;  // may be null
+    long long rows;
+    int cols;
+    int dtype;
+};
+
+// Enqueue the forward / backward / row-softmax kernels on `st`; return hipGetLastError()
+// of the launches.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
 
 // Query tiles per (batch, head) of the forward grid.
 long long fwd_grid_tiles(int N, int dtype);

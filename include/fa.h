@@ -32,6 +32,7 @@
  *     rounded to the input dtype (round to nearest even).  The fp32 path uses fp32
  *     MFMA throughout.
  *   - Supported: B, H, N >= 1; d in {64, 128}; B*H*ceil(N/64) < 2^31.
+ *   (fa_softmax_rows, below, has conventions of its own.)
  *   - Errors: arguments are validated before anything is enqueued; on failure a
  *     negative fa_status is returned and nothing runs.  A failed kernel launch returns
  *     FA_ERR_HIP.  Faults inside a kernel surface at the caller's next
@@ -52,7 +53,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = -1,        /* a required pointer is NULL */
-    FA_ERR_SHAPE = -2,       /* B, H or N < 1, or the grid would exceed 2^31 - 1 tiles */
+    FA_ERR_SHAPE = -2,       /* a size < 1, or the grid would exceed 2^31 - 1 workgroups */
     FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128} or unknown dtype */
     FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
     FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than fa_bwd_workspace_size() */
@@ -109,6 +110,28 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                  const float* lse, void* dq, void* dk, void* dv,
                  int B, int H, int N, int d, float scale, int causal, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * Row-wise softmax of a [rows, cols] array and the logsumexp of each row: the online
+ * softmax on its own ("How FlashAttention Actually Works" -- "The Secret Weapon: Online
+ * Softmax": subtract the row maximum before exponentiating, keep a running maximum and
+ * sum; "How does FlashAttention optimize memory and speed via tiling?" -- "Core Technical
+ * Innovations", item 2: the merge of two (max, sum) pairs).
+ *   y[r, c] = exp(x[r, c] - m_r) / l_r,  lse[r] = m_r + ln l_r,
+ *   m_r = max_c x[r, c],  l_r = sum_c exp(x[r, c] - m_r).
+ * x, y: DEVICE pointers to contiguous row-major [rows, cols] arrays of element type `dtype`
+ * (FA_F32 or FA_BF16), 16-byte aligned; rows need not start on 16-byte boundaries.  y may
+ * equal x (in place); no other overlap is allowed.  lse: DEVICE pointer to float [rows]
+ * (4-byte aligned), or NULL to skip it.  -inf entries are allowed and give exact zeros; a
+ * row whose entries are all -inf has no softmax and gets NaN outputs and a NaN lse.  x
+ * must hold no NaN or +inf.  Arithmetic in fp32; y is rounded to `dtype` (nearest even).
+ * A row that fits on chip (up to 16368 bf16 or 8184 fp32 values) is read from HBM once;
+ * longer rows are read twice (an online pass, then the normalising pass).
+ * Errors: FA_ERR_NULL (x or y NULL), FA_ERR_SHAPE (rows or cols < 1, rows > 2^31 - 1),
+ * FA_ERR_UNSUPPORTED (dtype), FA_ERR_ALIGN; nothing is enqueued on failure.  Enqueued on
+ * `stream`; no allocation, no synchronisation.
+ */
+int fa_softmax_rows(const void* x, void* y, float* lse, long long rows, int cols, int dtype, void* stream);
 
 /* A static, never-NULL description of a status code (unknown codes included). */
 const char* fa_status_string(int status);

@@ -79,3 +79,12 @@ def test_traffic_is_scaled_by_the_copy_kernel(tmp_path, monkeypatch):
     data["source_sha256"] = "0" * 64
     out.write_text(json.dumps(data))
     assert bench.load_traffic("synthetic") is None
+
+
+def test_softmax_units_and_digest():
+    """The row softmax moves x once and y once (plus one float of lse per row); its counter
+    summary is keyed to its own sources, so editing the attention kernels does not stale it."""
+    assert bench.softmax_bytes(65536, 8192, "bf16") == 2 * 65536 * 8192 * 2 + 4 * 65536
+    assert bench.softmax_bytes(3, 5, "f32") == 2 * 3 * 5 * 4 + 12
+    assert bench.is_softmax("softmax_bf16_r65536_c8192") and not bench.is_softmax("fwd_bf16_causal_b4h32_n8192_d128")
+    assert bench.sources_digest("softmax_bf16_r65536_c8192") != bench.sources_digest("fwd_bf16_causal_b4h32_n8192_d128")

@@ -34,7 +34,7 @@ def test_header_is_plain_c():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_status_string",
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string",
             "fa_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
@@ -155,3 +155,18 @@ def test_product_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def call_softmax(x=P, y=P, lse=P, rows=4, cols=100, dtype=1):
+    return fa.load_library().fa_softmax_rows(x, y, lse, rows, cols, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(y=None), -1),
+    (dict(rows=0), -2), (dict(cols=0), -2), (dict(rows=-3), -2), (dict(rows=1 << 31), -2),
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(x=P + 8), -4), (dict(y=P + 4), -4), (dict(lse=P + 2), -4),
+])
+def test_softmax_rejects_bad_arguments(kw, code):
+    """fa_softmax_rows validates before any HIP call (lse may be NULL; rows < 2^31)."""
+    assert call_softmax(**kw) == code

@@ -1,0 +1,115 @@
+"""GPU parity of fa_softmax_rows against the fp64 row-softmax oracle, through the C ABI.
+
+Small cases cover each path of the kernel (a 64-lane team per short row, a 256-lane team
+per row held in registers, the two-pass streaming path for longer rows) with ragged row
+counts, rows that start off 16-byte boundaries, -inf masks, rows with no finite entry, and
+in-place use; the bench workload runs at full size, compared on seeded row samples plus
+invariants over every row.
+
+Bounds: the stated ones (fp32 max-abs 1e-4; bf16 max-abs 2e-2 and mean-abs 2e-3), and for
+bf16 a tighter one derived from the arithmetic: outputs are computed in fp32 and rounded
+once to bf16, so |y - ref| <= 2^-9 |ref| (rounding) + 1e-6 |ref| (fp32 exp and division),
+written as 2^-8 |ref| + 1e-7."""
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+from tests.gpu_util import assert_parity, gpu_available, log, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def to_dev(case):
+    import torch
+    if case["dtype"] == "bf16":
+        host = torch.from_numpy(case["bits"].view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(np.ascontiguousarray(case["values"]))
+    return host.to("cuda").contiguous()
+
+
+def run(case, in_place=False, with_lse=True):
+    import torch
+    import exact_io_aware_70_amd as fa
+    x = to_dev(case)
+    y, lse = fa.fa_softmax_rows(x, y=x if in_place else None, with_lse=with_lse)
+    torch.cuda.synchronize()
+    return y, lse
+
+
+def compare(case, y, lse, label):
+    log(f"[softmax] {label}")
+    ref_y, ref_lse = oracle.softmax_rows(case["values"])
+    got_y = to_f64(y)
+    empty = np.isnan(ref_lse)
+    # Rows with no finite entry: NaN throughout, as the definition evaluates.
+    assert np.array_equal(np.isnan(got_y).all(axis=1), empty) and not np.isnan(got_y[~empty]).any()
+    assert_parity("y", got_y[~empty], ref_y[~empty], case["dtype"])
+    if case["dtype"] == "bf16":
+        excess = np.abs(got_y[~empty] - ref_y[~empty]) - (2.0 ** -8 * np.abs(ref_y[~empty]) + 1e-7)
+        assert excess.max(initial=-1.0) <= 0, f"y: exceeds 2^-8 |ref| + 1e-7 by {excess.max():.3e}"
+    if lse is not None:
+        got_lse = to_f64(lse)
+        assert np.array_equal(np.isnan(got_lse), empty)
+        assert_parity("lse", got_lse[~empty], ref_lse[~empty], case["dtype"])
+
+
+# (rows, cols) per path; bf16 vectors hold 8 values, fp32 vectors 4, so the thresholds differ.
+SHAPES = [(1, 1), (3, 7), (5, 17), (37, 1000), (6, 1016), (6, 1017), (9, 2040), (9, 2047), (7, 4097),
+          (4, 8184), (3, 8185), (4, 16368), (3, 16369), (2, 70001), (1001, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_softmax_shapes(dtype, rows, cols):
+    case = fa_inputs.make_softmax_case(rows, cols, dtype, seed=200 + rows + cols, x_scale=3.0)
+    y, lse = run(case)
+    compare(case, y, lse, f"{dtype} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mask", ["causal", "empty-rows"])
+@pytest.mark.parametrize("cols", [33, 3000, 20000])
+def test_softmax_masks(dtype, mask, cols):
+    case = fa_inputs.make_softmax_case(29, cols, dtype, seed=300 + cols, mask=mask)
+    y, lse = run(case)
+    compare(case, y, lse, f"{dtype} 29x{cols} mask={mask}")
+
+
+@pytest.mark.parametrize("cols", [1000, 9000, 30000])
+def test_softmax_in_place_without_lse(cols):
+    case = fa_inputs.make_softmax_case(11, cols, "bf16", seed=400 + cols)
+    y, lse = run(case, in_place=True, with_lse=False)
+    assert lse is None
+    compare(case, y, None, f"bf16 11x{cols} in place, no lse")
+
+
+def test_softmax_large_logits_f32():
+    """Logits spread over +-100: subtracting the maximum keeps every exponential finite."""
+    case = fa_inputs.make_softmax_case(64, 5000, "f32", seed=500, x_scale=30.0)
+    y, lse = run(case)
+    compare(case, y, lse, "f32 64x5000 x30")
+
+
+@pytest.mark.parametrize("name", list(fa_inputs.SOFTMAX_CONFIGS))
+def test_softmax_workload_full_size(name):
+    """The named workload at full size in the bench's launch configuration: 512 seeded rows
+    against the oracle; every row sums to 1 and its lse lies in [max, max + ln cols]."""
+    import torch
+    c = fa_inputs.SOFTMAX_CONFIGS[name]
+    case = fa_inputs.make_softmax_case(c["rows"], c["cols"], c["dtype"], c["seed"], c["x_scale"])
+    x = to_dev(case)
+    y, lse = run(case)
+    rows = np.sort(np.random.default_rng(c["seed"] + 1000).choice(c["rows"], 512, replace=False))
+    sub = {"dtype": case["dtype"], "values": case["values"][rows],
+           "bits": None if case["bits"] is None else case["bits"][rows]}
+    compare(sub, y[torch.from_numpy(rows).cuda()], lse[torch.from_numpy(rows).cuda()], f"{name} (512 rows)")
+    sums = y.double().sum(dim=1)
+    mx = x.float().amax(dim=1).double()
+    tol = 2.0 ** -8 if c["dtype"] == "bf16" else 1e-5
+    log(f"  row sums in [{sums.min().item():.6f}, {sums.max().item():.6f}]")
+    assert float((sums - 1).abs().max()) <= tol
+    l64 = lse.double()
+    assert bool(((l64 >= mx - 1e-4) & (l64 <= mx + np.log(c["cols"]) + 1e-4)).all())
