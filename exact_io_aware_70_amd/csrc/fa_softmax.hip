@@ -13,9 +13,9 @@
 // contiguous KiB.  Rows need not start on a 16-byte boundary: the first and last vectors
 // of a row may hold a neighbour's elements, which are masked to -inf on load and never
 // stored (those two vectors are stored element by element).
-//   - Cached path (the row fits in the team's registers): the row is read once, its
-//     maximum and sum reduced over the team, and the outputs written from registers: one
-//     HBM read and one write per element.
+//   - Cached path (the row fits in the team's registers): the row is read once and kept as
+//     raw 16-byte words, its maximum and sum reduced over the team, and the outputs
+//     written from registers: one HBM read and one write per element.
 //   - Streaming path (longer rows): each lane folds its vectors into a running (max, sum)
 //     pair chunk by chunk with the merge above, the team merges the lanes' pairs the same
 //     way, and a second pass re-reads the row to write the outputs.
@@ -72,11 +72,22 @@ struct Vec16<__bf16> {
     }
 };
 
+// -inf in each element of a vector, as raw bits.
+template <typename T>
+__device__ __forceinline__ uint32_t neg_inf_word();
+template <>
+__device__ __forceinline__ uint32_t neg_inf_word<float>() { return 0xff800000u; }
+template <>
+__device__ __forceinline__ uint32_t neg_inf_word<__bf16>() { return 0xff80ff80u; }
+
 // One row as seen by its team: flat element range [e0, e1) of an array of `total`
 // elements, vectors v0 .. v0 + nv - 1 (vector v covers elements v * VE .. v * VE + VE - 1).
+// Vectors are kept as raw 16-byte words (4 registers each) and unpacked to fp32 only while
+// a pass works on them; entries outside the row hold the bits of -inf.
 template <typename T>
 struct Row {
     static constexpr int VE = Vec16<T>::VE;
+    static constexpr int EB = 16 / VE * 8;  // bits per element
     long long e0, e1, total, v0;
     int nv;
     __device__ Row(long long r, int cols, long long rows) {
@@ -86,28 +97,51 @@ struct Row {
         v0 = e0 / VE;
         nv = (int)((e1 - 1) / VE - v0 + 1);
     }
-    // Vector j of the row as floats, entries outside the row set to -inf.  Whole vectors are
-    // read with one 16-byte load; only the array's last vector, which may run past the end
-    // of the allocation, is read element by element.
-    __device__ void load(const T* x, int j, float (&f)[VE]) const {
-        const long long vb = (v0 + j) * VE;
-        if (vb + VE <= total) {
-            Vec16<T>::unpack(*reinterpret_cast<const u32x4*>(x + vb), f);
+    // Replace the bits of element e of a raw vector by those of -inf.
+    __device__ static void mask_elem(u32x4& w, int e) {
+        if constexpr (VE == 4) {
+            w[e] = 0xff800000u;
         } else {
+            const int k = e >> 1, sh = (e & 1) * 16;
+            w[k] = (w[k] & ~(0xffffu << sh)) | (0xff80u << sh);
+        }
+    }
+    // Vector j of the row, raw, entries outside the row set to -inf.  Whole vectors are read
+    // with one 16-byte load; only the array's last vector, which may run past the end of the
+    // allocation, is read element by element.
+    __device__ u32x4 load(const T* x, int j) const {
+        const long long vb = (v0 + j) * VE;
+        u32x4 w;
+        if (vb + VE <= total) {
+            w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + vb));
+        } else {
+            const uint32_t ni = neg_inf_word<T>();
+            w = u32x4{ni, ni, ni, ni};
+            const uint16_t* xs = reinterpret_cast<const uint16_t*>(x + vb);
+            const uint32_t* xw = reinterpret_cast<const uint32_t*>(x + vb);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) f[e] = (vb + e < total) ? Vec16<T>::get(x + vb + e) : -INFINITY;
+            for (int e = 0; e < VE; ++e)
+                if (vb + e < total) {
+                    if constexpr (VE == 4) {
+                        w[e] = xw[e];
+                    } else {
+                        const int k = e >> 1, sh = (e & 1) * 16;
+                        w[k] = (w[k] & ~(0xffffu << sh)) | ((uint32_t)xs[e] << sh);
+                    }
+                }
         }
         if (vb < e0 || vb + VE > e1) {
 #pragma unroll
             for (int e = 0; e < VE; ++e)
-                if (vb + e < e0 || vb + e >= e1) f[e] = -INFINITY;
+                if (vb + e < e0 || vb + e >= e1) mask_elem(w, e);
         }
+        return w;
     }
     // Store the entries of vector j that belong to the row.
     __device__ void store(T* y, int j, const float (&f)[VE]) const {
         const long long vb = (v0 + j) * VE;
         if (vb >= e0 && vb + VE <= e1) {
-            *reinterpret_cast<u32x4*>(y + vb) = Vec16<T>::pack(f);
+            __builtin_nontemporal_store(Vec16<T>::pack(f), reinterpret_cast<u32x4*>(y + vb));
         } else {
 #pragma unroll
             for (int e = 0; e < VE; ++e)
@@ -144,7 +178,24 @@ __device__ __forceinline__ float team_sum(float v, float* red) {
     return v;
 }
 
-// KV vectors per lane are cached (STREAM = false: the whole row; STREAM = true: one chunk
+template <typename T>
+__device__ __forceinline__ float vmax(u32x4 w, float m) {
+    float f[Vec16<T>::VE];
+    Vec16<T>::unpack(w, f);
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::VE; ++e) m = fmaxf(m, f[e]);
+    return m;
+}
+template <typename T>
+__device__ __forceinline__ float vsum_exp(u32x4 w, float ms, float s) {
+    float f[Vec16<T>::VE];
+    Vec16<T>::unpack(w, f);
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::VE; ++e) s += fast_exp2(fmaf(f[e], kLog2e, -ms));
+    return s;
+}
+
+// KV raw vectors per lane are held (STREAM = false: the whole row; STREAM = true: one chunk
 // at a time).  Each 256-thread workgroup serves 256 / TEAM rows.
 template <typename T, int TEAM, int KV, bool STREAM>
 __global__ __launch_bounds__(256) void softmax_rows_kernel(const T* __restrict__ x, T* __restrict__ y,
@@ -158,54 +209,38 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(const T* __restrict__
     // and TEAM = 64 reductions stay inside the wave, so no barrier is left waiting.
     if (r >= rows) return;
     const Row<T> row(r, cols, rows);
+    const uint32_t ni = neg_inf_word<T>();
 
-    float f[KV][VE];
+    u32x4 w[KV];
     float m = kNegBig, l = 0.f;
     if constexpr (!STREAM) {
 #pragma unroll
         for (int j = 0; j < KV; ++j) {
             const int idx = t + j * TEAM;
-            if (idx < row.nv) {
-                row.load(x, idx, f[j]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VE; ++e) f[j][e] = -INFINITY;
-            }
-#pragma unroll
-            for (int e = 0; e < VE; ++e) m = fmaxf(m, f[j][e]);
+            w[j] = idx < row.nv ? row.load(x, idx) : u32x4{ni, ni, ni, ni};
         }
+#pragma unroll
+        for (int j = 0; j < KV; ++j) m = vmax<T>(w[j], m);
         m = team_max<TEAM>(m, red);
         const float ms = m * kLog2e;
 #pragma unroll
-        for (int j = 0; j < KV; ++j)
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                f[j][e] = fast_exp2(fmaf(f[j][e], kLog2e, -ms));
-                l += f[j][e];
-            }
+        for (int j = 0; j < KV; ++j) l = vsum_exp<T>(w[j], ms, l);
         l = team_sum<TEAM>(l, red);
     } else {
         // Pass 1: this lane's running (max, sum) over its vectors, chunk by chunk.
         for (int c0 = 0; c0 < row.nv; c0 += KV * TEAM) {
-            float cm = kNegBig;
 #pragma unroll
             for (int j = 0; j < KV; ++j) {
                 const int idx = c0 + t + j * TEAM;
-                if (idx < row.nv) {
-                    row.load(x, idx, f[j]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) f[j][e] = -INFINITY;
-                }
-#pragma unroll
-                for (int e = 0; e < VE; ++e) cm = fmaxf(cm, f[j][e]);
+                w[j] = idx < row.nv ? row.load(x, idx) : u32x4{ni, ni, ni, ni};
             }
+            float cm = kNegBig;
+#pragma unroll
+            for (int j = 0; j < KV; ++j) cm = vmax<T>(w[j], cm);
             const float mn = fmaxf(m, cm), ms = mn * kLog2e;
             float s = 0.f;
 #pragma unroll
-            for (int j = 0; j < KV; ++j)
-#pragma unroll
-                for (int e = 0; e < VE; ++e) s += fast_exp2(fmaf(f[j][e], kLog2e, -ms));
+            for (int j = 0; j < KV; ++j) s = vsum_exp<T>(w[j], ms, s);
             l = l * fast_exp2((m - mn) * kLog2e) + s;
             m = mn;
         }
@@ -219,57 +254,54 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(const T* __restrict__
     const bool empty = !(l > 0.f);
     const float inv = empty ? __builtin_nanf("") : 1.0f / l;
     if (lse && t == 0) lse[r] = empty ? __builtin_nanf("") : m + __logf(l);
+    const float ms = m * kLog2e;
 
-    if constexpr (!STREAM) {
+    // Write the normalised row (the streaming path re-reads it first).
+    for (int c0 = 0; c0 < (STREAM ? row.nv : 1); c0 += KV * TEAM) {
+        if constexpr (STREAM) {
 #pragma unroll
-        for (int j = 0; j < KV; ++j) {
-            const int idx = t + j * TEAM;
-            if (idx < row.nv) {
-#pragma unroll
-                for (int e = 0; e < VE; ++e) f[j][e] *= inv;
-                row.store(y, idx, f[j]);
+            for (int j = 0; j < KV; ++j) {
+                const int idx = c0 + t + j * TEAM;
+                if (idx < row.nv) w[j] = row.load(x, idx);
             }
         }
-    } else {
-        // Pass 2: re-read and write the normalised row.
-        const float ms = m * kLog2e;
-        for (int c0 = 0; c0 < row.nv; c0 += KV * TEAM) {
 #pragma unroll
-            for (int j = 0; j < KV; ++j) {
-                const int idx = c0 + t + j * TEAM;
-                if (idx < row.nv) row.load(x, idx, f[j]);
-            }
+        for (int j = 0; j < KV; ++j) {
+            const int idx = c0 + t + j * TEAM;
+            if (idx < row.nv) {
+                float f[VE];
+                Vec16<T>::unpack(w[j], f);
 #pragma unroll
-            for (int j = 0; j < KV; ++j) {
-                const int idx = c0 + t + j * TEAM;
-                if (idx < row.nv) {
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) f[j][e] = fast_exp2(fmaf(f[j][e], kLog2e, -ms)) * inv;
-                    row.store(y, idx, f[j]);
-                }
+                for (int e = 0; e < VE; ++e) f[e] = fast_exp2(fmaf(f[e], kLog2e, -ms)) * inv;
+                row.store(y, idx, f);
             }
         }
     }
 }
 
+// Launch shape by row length: short rows get one wave each (four rows per workgroup, no
+// barriers); longer rows a whole workgroup holding as few vectors per lane as the row needs
+// (fewer registers, more workgroups per CU, more bytes in flight); rows past 2048 vectors
+// stream.  Measured on the 65536 x 8192 bf16 workload: 5 vectors per lane beat 8 (5.8 vs
+// 5.2 TB/s), and non-temporal loads and stores (the data is touched once) add 6%.
+template <typename T, int TEAM, int KV, bool STREAM>
+hipError_t launch_shape(const SoftmaxArgs& a, hipStream_t st) {
+    constexpr int RPW = 256 / TEAM;
+    const long long grid = (a.rows + RPW - 1) / RPW;
+    hipLaunchKernelGGL((softmax_rows_kernel<T, TEAM, KV, STREAM>), dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const T*>(a.x), static_cast<T*>(a.y), a.lse, a.rows, a.cols);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_softmax_t(const SoftmaxArgs& a, hipStream_t st) {
-    constexpr int VE = Vec16<T>::VE;
-    const long long nv_max = a.cols / VE + 2;  // vectors a row can touch
-    const T* x = static_cast<const T*>(a.x);
-    T* y = static_cast<T*>(a.y);
-    if (nv_max <= 64 * 4) {
-        const long long grid = (a.rows + 3) / 4;
-        hipLaunchKernelGGL((softmax_rows_kernel<T, 64, 4, false>), dim3((unsigned)grid), dim3(256), 0, st, x, y,
-                           a.lse, a.rows, a.cols);
-    } else if (nv_max <= 256 * 8) {
-        hipLaunchKernelGGL((softmax_rows_kernel<T, 256, 8, false>), dim3((unsigned)a.rows), dim3(256), 0, st, x, y,
-                           a.lse, a.rows, a.cols);
-    } else {
-        hipLaunchKernelGGL((softmax_rows_kernel<T, 256, 8, true>), dim3((unsigned)a.rows), dim3(256), 0, st, x, y,
-                           a.lse, a.rows, a.cols);
-    }
-    return hipGetLastError();
+    const long long nv_max = a.cols / Vec16<T>::VE + 2;  // vectors a row can touch
+    if (nv_max <= 64 * 4) return launch_shape<T, 64, 4, false>(a, st);
+    if (nv_max <= 256 * 2) return launch_shape<T, 256, 2, false>(a, st);
+    if (nv_max <= 256 * 3) return launch_shape<T, 256, 3, false>(a, st);
+    if (nv_max <= 256 * 5) return launch_shape<T, 256, 5, false>(a, st);
+    if (nv_max <= 256 * 8) return launch_shape<T, 256, 8, false>(a, st);
+    return launch_shape<T, 256, 8, true>(a, st);
 }
 
 }  // namespace

@@ -57,7 +57,8 @@ def compare(case, y, lse, label):
 
 
 # (rows, cols) per path; bf16 vectors hold 8 values, fp32 vectors 4, so the thresholds differ.
-SHAPES = [(1, 1), (3, 7), (5, 17), (37, 1000), (6, 1016), (6, 1017), (9, 2040), (9, 2047), (7, 4097),
+SHAPES = [(1, 1), (3, 7), (5, 17), (37, 1000), (6, 1016), (6, 1017), (9, 2040), (9, 2047), (5, 3000), (7, 4097),
+          (5, 6000), (6, 10000),
           (4, 8184), (3, 8185), (4, 16368), (3, 16369), (2, 70001), (1001, 64)]
 
 
