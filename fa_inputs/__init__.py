@@ -47,6 +47,12 @@ CONFIGS = {
                                              d=128, causal=True, seed=5, q_scale=1.0),
 }
 
+FP8_CONFIGS = {
+    # The bf16 bench workload's draws (same seed and Q scale), quantised to E4M3 per head.
+    "fwd_fp8_causal_b4h32_n8192_d128": dict(B=4, H=32, N=8192, d=128, causal=True, seed=3, q_scale=3.0),
+    "fwd_fp8_b4h8_n2048_d128": dict(B=4, H=8, N=2048, d=128, causal=False, seed=6, q_scale=1.0),
+}
+
 SOFTMAX_CONFIGS = {
     "softmax_bf16_r65536_c8192": dict(dtype="bf16", rows=65536, cols=8192, seed=11, x_scale=1.0),
     "softmax_f32_r8192_c2048": dict(dtype="f32", rows=8192, cols=2048, seed=12, x_scale=1.0),
@@ -144,3 +150,27 @@ def make_softmax_case(rows: int, cols: int, dtype: str, seed: int, x_scale: floa
         bits = bf16_bits(x)
         return {"dtype": dtype, "shape": (rows, cols), "bits": bits, "values": bf16_bits_to_f32(bits)}
     return {"dtype": dtype, "shape": (rows, cols), "bits": None, "values": x}
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP E4M3 (nearest, ties to even) and return the uint8 codes.
+
+    Input preparation only: the conversion is torch's float8_e4m3fn cast on the CPU."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def make_fp8_case(B: int, H: int, N: int, d: int, seed: int, q_scale: float = 1.0) -> dict:
+    """Inputs of one FP8 forward case: Q, K, V drawn as in ``make_case`` (float32), then each
+    (b, h) of each tensor scaled so its largest magnitude maps to 448 (the largest E4M3
+    value) and rounded to E4M3.  Returns ``{"shape", "scale", name: {"codes": uint8
+    [B,H,N,d], "descale": float32 [B,H]}}``; the value of a code is decode(code) * descale."""
+    raw = draw((B, H, N, d), seed, ("q", "k", "v"), q_scale)
+    case = {"shape": (B, H, N, d), "scale": 1.0 / math.sqrt(d)}
+    for name, x in raw.items():
+        amax = np.abs(x).reshape(B, H, -1).max(axis=2)
+        sc = (np.float32(448.0) / np.maximum(amax, np.float32(1e-30))).astype(np.float32)
+        codes = e4m3_codes(x * sc[:, :, None, None])
+        case[name] = {"codes": codes, "descale": (np.float32(1.0) / sc).astype(np.float32)}
+    return case

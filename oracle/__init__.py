@@ -11,3 +11,4 @@ inputs, finite differences and a library special case); none is "parity unpinned
 from .attention import backward, forward, forward_rows, probabilities, scores  # noqa: F401
 from .online import chunk_merge, tiled_forward  # noqa: F401
 from .softmax import softmax_rows  # noqa: F401
+from .fp8 import decode_e4m3, forward_fp8  # noqa: F401
