@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --workload softmax_bf16_r65536_c8192   (the row-softmax kernel on its own)
+    python bench.py --workload fwd_fp8_causal_b4h32_n8192_d128   (the E4M3 forward)
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--copy-mib M] [--workload NAME]
     python bench.py --summarize-sq STATS_CSV PMC_DIR [PMC_DIR ...] [--workload NAME]
 
@@ -40,9 +41,11 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
 KERNEL_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd.hip", "exact_io_aware_70_amd/csrc/fa_bwd.hip",
                   "exact_io_aware_70_amd/csrc/fa_device.h"]
 SOFTMAX_SOURCES = ["exact_io_aware_70_amd/csrc/fa_softmax.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
+FP8_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
 
 
 def parse():
@@ -77,10 +80,14 @@ def is_softmax(workload) -> bool:
     return workload.startswith("softmax_")
 
 
+def is_fp8(workload) -> bool:
+    return workload.startswith("fwd_fp8_")
+
+
 def sources_digest(workload="") -> str:
     """SHA-256 of the kernel sources a workload runs (the counter summaries record it)."""
     h = hashlib.sha256()
-    for path in (SOFTMAX_SOURCES if is_softmax(workload) else KERNEL_SOURCES):
+    for path in (SOFTMAX_SOURCES if is_softmax(workload) else FP8_SOURCES if is_fp8(workload) else KERNEL_SOURCES):
         with open(os.path.join(ROOT, path), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -146,7 +153,7 @@ def summarize_pmc(args):
 
     ff, fw = calib(fetch), calib(write)
     names = ["fwd_bf16_kernel", "fwd_f32_kernel", "delta_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
-             "dq_bf16_kernel", "dq_f32_kernel", "softmax_rows_kernel"]
+             "dq_bf16_kernel", "dq_f32_kernel", "softmax_rows_kernel", "fwd_fp8_kernel"]
     out = {}
     for short in names:
         fv = [v for (_, n), v in fetch.items() if short in n]
@@ -303,6 +310,110 @@ def cpu_softmax_baseline(case, rows):
                                         f"same byte formula as value", "seconds": round(t, 3)}
 
 
+def cpu_fp8_baseline(case, causal, heads):
+    """The fp64 FP8 oracle (as it stands) on `heads` heads of the workload: decode + forward."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    B0, H0, N, d = case["shape"]
+    heads = min(heads, B0 * H0)
+    sel = [(b, h) for b in range(B0) for h in range(H0)][:heads]
+    t = 0.0
+    for b, h in sel:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        args = [case[n]["codes"][sl] for n in ("q", "k", "v")] + [case[n]["descale"][sl] for n in ("q", "k", "v")]
+        t0 = time.perf_counter()
+        oracle.forward_fp8(*args, case["scale"], causal)
+        t += time.perf_counter() - t0
+    ff, _ = flops(1, heads, N, d, causal)
+    return {"value": round(ff / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {B0 * H0} heads, full N={N}, d={d}: fp64 decode + forward with explicit S and P "
+                      f"({t:.1f} s); same flop formula as value", "seconds": round(t, 3)}
+
+
+def bench_fp8(args):
+    """One step = one fa_fwd_fp8 launch (E4M3 Q, K, V with per-head descales; bf16 O)."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_70_amd as fa
+    import fa_inputs
+
+    c = fa_inputs.FP8_CONFIGS[args.workload]
+    B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
+    case = fa_inputs.make_fp8_case(B, H, N, d, c["seed"], c["q_scale"])
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(case[n]["codes"]).to(dev) for n in ("q", "k", "v")}
+    ds = {n: torch.from_numpy(case[n]["descale"]).to(dev) for n in ("q", "k", "v")}
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib * (1 << 20), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        fa.fa_fwd_fp8(t["q"], t["k"], t["v"], ds["q"], ds["k"], ds["v"], o, lse, scale=case["scale"],
+                      causal=causal, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in events:
+        ev[0].record(stream)
+        step()
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[0].elapsed_time(ev[1]) for ev in events]
+    avg = float(np.mean(ms))
+    ff, _ = flops(B, H, N, d, causal)
+    ms_step = wall * 1e3 / args.steps
+    ach = ff / (avg * 1e-3) / 1e12
+    traffic = load_traffic(args.workload)
+    tb = traffic.get("fwd_fp8_kernel", {}).get("bytes") if traffic else None
+    out = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved), E4M3 inputs",
+        "value": round(ff / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) Q/K/V, Q x%g, quantised to E4M3 per head)" % c["q_scale"],
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal, "pass": "fwd",
+                   "step_flops": ff},
+        "kernels": {"fwd_fp8_kernel": {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "bound": "mfma",
+                                       "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(ach / PEAK_FP8_TFLOPS, 4), "units_per_launch": ff,
+                                       "traffic": tb}},
+        "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": tb,
+                     "launch_ms": round(avg, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_fp8_baseline(case, causal, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
 def bench_softmax(args):
     """One step = one fa_softmax_rows launch over the whole [rows, cols] array."""
     import numpy as np
@@ -393,6 +504,9 @@ def main():
 
     if is_softmax(args.workload):
         bench_softmax(args)
+        return
+    if is_fp8(args.workload):
+        bench_fp8(args)
         return
 
     import numpy as np

@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp,
                                  ctypes.POINTER(vp)]
     lib.fa_bwd_timed.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_softmax_rows.argtypes = [vp, vp, vp, ctypes.c_longlong, i, i, vp]
     lib.fa_softmax_rows.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -209,3 +211,32 @@ def fa_softmax_rows(x, y=None, lse=None, with_lse=True, stream=None):
     if st != FA_OK:
         raise FAError(st, "fa_softmax_rows")
     return y, lse
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, scale=None, causal=False,
+               stream=None):
+    """FP8 forward: q8, k8, v8 are uint8 E4M3 codes [B,H,N,d] (or torch.float8_e4m3fn);
+    the descales are float32 [B,H].  Returns (o [B,H,N,d] bfloat16, lse [B,H,N] float32)."""
+    import torch
+    lib = load_library()
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    B, H, N, d = q8.shape
+    dev = q8.device
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name}: dtype {t.dtype}, expected uint8 codes or float8_e4m3fn")
+        _check(name, t, (B, H, N, d), t.dtype, dev)
+    for name, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        _check(name, t, (B, H), torch.float32, dev)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check("o", o, (B, H, N, d), torch.bfloat16, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+                        v_descale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, sc, 1 if causal else 0,
+                        _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
+    return o, lse

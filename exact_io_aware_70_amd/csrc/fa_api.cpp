@@ -85,6 +85,21 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                       workspace_bytes, stream, events);
 }
 
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale, const float* k_descale,
+               const float* v_descale, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+               void* stream) {
+    if (!q8 || !k8 || !v8 || !q_descale || !k_descale || !v_descale || !o || !lse) return FA_ERR_NULL;
+    const int st = check_common(B, H, N, d, scale, FA_BF16);
+    if (st != FA_OK) return st;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(v_descale, 4))
+        return FA_ERR_ALIGN;
+    fa::Fp8FwdArgs a{q8, k8, v8, q_descale, k_descale, v_descale, o, lse, B, H, N, d, scale, causal ? 1 : 0};
+    const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_softmax_rows(const void* x, void* y, float* lse, long long rows, int cols, int dtype, void* stream) {
     if (!x || !y) return FA_ERR_NULL;
     // One workgroup per row at most: keep the 1-D grid in range.

@@ -40,6 +40,20 @@ struct BwdArgs {
     void* const* events;  // optional: hipEvent_t recorded before each launch and after the last
 };
 
+struct Fp8FwdArgs {
+    const void* q;  // E4M3 codes [B, H, N, d]
+    const void* k;
+    const void* v;
+    const float* q_descale;  // [B, H]
+    const float* k_descale;
+    const float* v_descale;
+    void* o;  // bf16 [B, H, N, d]
+    float* lse;
+    int B, H, N, d;
+    float scale;
+    int causal;
+};
+
 struct SoftmaxArgs {
     const void* x;
     void* y;
@@ -54,6 +68,7 @@ struct SoftmaxArgs {
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t st);
 
 // Query tiles per (batch, head) of the forward grid.
 long long fwd_grid_tiles(int N, int dtype);

@@ -112,6 +112,27 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * FP8 forward pass: the same tiled online-softmax forward as fa_fwd over OCP E4M3 inputs,
+ * with both products on the FP8 matrix cores ("Breaking the Memory Wall" -- "The
+ * Solution: IO-Awareness & Tiling", items 1-2; "How does FlashAttention optimize memory
+ * and speed via tiling?" -- "Interview tips" names FP8 support as a FlashAttention-3
+ * addition).
+ *   q8, k8, v8: DEVICE pointers to E4M3 codes (1 byte each) [B, H, N, d], 16-byte aligned;
+ *     the value of a code of head (b, h) is decode(code) * X_descale[b * H + h].
+ *   q_descale, k_descale, v_descale: DEVICE pointers to float [B, H].
+ *   o: DEVICE pointer to bf16 [B, H, N, d]; lse: float [B, H, N], the natural-log logsumexp
+ *     of scale * (descaled Q) (descaled K)^T over the visible keys.
+ * Arithmetic: Q8 K8^T on E4M3 MFMA with fp32 accumulation, times scale * q_descale *
+ * k_descale; probabilities exp(s - m) (m a running reference within 8 log2 units of the row
+ * maximum, so they stay <= 256) rounded to E4M3 (nearest even) for the P V product and for
+ * the row sum; O = (P8 V8) * v_descale / sum(P8), rounded to bf16.
+ * Supported: d = 128 only (FA_ERR_UNSUPPORTED otherwise); other conventions as fa_fwd.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale, const float* k_descale,
+               const float* v_descale, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+               void* stream);
+
+/*
  * Row-wise softmax of a [rows, cols] array and the logsumexp of each row: the online
  * softmax on its own ("How FlashAttention Actually Works" -- "The Secret Weapon: Online
  * Softmax": subtract the row maximum before exponentiating, keep a running maximum and

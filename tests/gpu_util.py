@@ -98,3 +98,40 @@ def assert_parity(what: str, got, ref, dtype: str, cond=None) -> tuple[float, fl
     if tol["mean_abs"] is not None:
         assert mean <= tol["mean_abs"], f"{what}: mean-abs {mean:.3e} > {tol['mean_abs']:.1e}"
     return mx, mean
+
+
+def fp8_forward_bounds(q, k, v, scale: float, causal: bool, rows=None):
+    """Per-element error bounds of the FP8 forward for one head, in fp64 from oracle values.
+
+    The kernel rounds each probability P~_k (in [0, 256]) to E4M3 for the P V product and
+    the row sum: a normal value moves by at most 2^-4 P~_k, a subnormal one (below 2^-6) by
+    at most 2^-10.  With l~ = sum_k P~_k, the first-order change of O = sum P8 V / sum P8 is
+    sum_k dP~_k (V_k - O) / l~.  The kernel's reference maximum never exceeds the row's true
+    maximum, so l~ >= l, the sum of exp(s - max) the oracle computes, and
+        |dO_c| <= sum_k (2^-4 P_k + 2^-10 / l) |V_kc - O_c|,
+        |dlse| <= sum_k (2^-4 P_k + 2^-10 / l)   (lse = m + ln sum P8).
+    The bf16 store adds BF16_U |O_c| = 2^-8 |O_c|.  Returned: (bound_O, sigma_O, bound_lse) for the given
+    query rows (default all), where sigma_O is the standard deviation of the same error
+    under independent roundings uniform in their half-ulp intervals (a mean-error scale).
+    """
+    from oracle import attention as oracle
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = scale * (q[idx] @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > idx[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    o = p @ v
+    vis = np.isfinite(s)
+    c = np.where(vis, 2.0 ** -4 * p + 2.0 ** -10 / l, 0.0)  # [R, N] per-key coefficient
+    bound = np.empty_like(o)
+    var = np.empty_like(o)
+    for col in range(v.shape[1]):
+        dv = np.abs(v[None, :, col] - o[:, col:col + 1])  # [R, N]
+        bound[:, col] = (c * dv).sum(axis=1)
+        var[:, col] = ((c * dv) ** 2).sum(axis=1) / 3.0
+    var += (BF16_U * np.abs(o)) ** 2 / 3.0
+    return bound + BF16_U * np.abs(o), np.sqrt(var), c.sum(axis=1)

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path()),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_is_plain_c():
@@ -34,7 +34,7 @@ def test_header_is_plain_c():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string",
+    assert {"fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string",
             "fa_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
@@ -170,3 +170,28 @@ def call_softmax(x=P, y=P, lse=P, rows=4, cols=100, dtype=1):
 def test_softmax_rejects_bad_arguments(kw, code):
     """fa_softmax_rows validates before any HIP call (lse may be NULL; rows < 2^31)."""
     assert call_softmax(**kw) == code
+
+
+def call_fp8(ptrs=None, **kw):
+    a = dict(GOOD, **kw)
+    p = dict(q=P, k=P, v=P, qd=P, kd=P, vd=P, o=P, lse=P)
+    p.update(ptrs or {})
+    return fa.load_library().fa_fwd_fp8(p["q"], p["k"], p["v"], p["qd"], p["kd"], p["vd"], p["o"], p["lse"],
+                                        a["B"], a["H"], a["N"], 128 if "d" not in kw else a["d"], a["scale"],
+                                        a["causal"], None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "qd", "kd", "vd", "o", "lse"])
+def test_fp8_null(which):
+    assert call_fp8(ptrs={which: None}) == -1
+
+
+@pytest.mark.parametrize("kw,code", [(dict(N=0), -2), (dict(B=0), -2), (dict(d=64), -3), (dict(d=96), -3),
+                                     (dict(scale=0.0), -3)])
+def test_fp8_bad_sizes(kw, code):
+    assert call_fp8(**kw) == code
+
+
+@pytest.mark.parametrize("which,off", [("q", 8), ("o", 4), ("lse", 2), ("qd", 2)])
+def test_fp8_misaligned(which, off):
+    assert call_fp8(ptrs={which: P + off}) == -4
