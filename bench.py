@@ -146,10 +146,12 @@ def summarize_pmc(args):
     copy_bytes = args.copy_mib * (1 << 20)
 
     def calib(per):
+        # The calibration copy is the largest copy kernel of the run (uploads of the inputs
+        # may also run as small copy kernels).
         vals = [v for (_, name), v in per.items() if "copyBuffer" in name]
         if not vals or copy_bytes <= 0:
             raise SystemExit("no copy kernel in the counter runs (run them with --copy-mib)")
-        return copy_bytes / (vals[0] * 1024.0)
+        return copy_bytes / (max(vals) * 1024.0)
 
     ff, fw = calib(fetch), calib(write)
     names = ["fwd_bf16_kernel", "fwd_f32_kernel", "delta_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
@@ -181,7 +183,7 @@ def summarize_pmc(args):
 
 def read_counters(dirs):
     """Mean per dispatch of every counter, per kernel (short name), over rocprofv3 --pmc folders."""
-    names = ["fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel"]
+    names = ["fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"]
     per = {}  # (short, counter) -> {dispatch: value}
     for d in dirs:
         for dp, _, files in os.walk(d):
@@ -208,19 +210,26 @@ def summarize_sq(args):
     The chip has 256 CUs of 4 SIMDs in 8 XCDs; GRBM_GUI_ACTIVE is summed over the XCDs, so
     one XCD's busy cycles are an eighth of it, and the clock is those cycles over the kernel's
     average duration (from the kernel-trace statistics given first).  A 32x32x16 bf16 MFMA
-    keeps its SIMD's matrix core busy for 32 cycles (SQ_VALU_MFMA_BUSY_CYCLES counts exactly
-    that), so MFMA busy = busy cycles / (1024 SIMDs x cycles)."""
+    keeps its SIMD's matrix core busy for 32 cycles and a 32x32x64 fp8 one for 64
+    (SQ_VALU_MFMA_BUSY_CYCLES counts exactly that), so MFMA busy = busy cycles / (1024 SIMDs
+    x cycles)."""
     stats_csv, dirs = args.summarize_sq[0], args.summarize_sq[1:]
     dur = {}
     with open(stats_csv) as f:
         for r in csv.DictReader(f):
-            for n in ("fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel"):
+            for n in ("fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"):
                 if n in r["Name"]:
                     dur[n] = float(r["AverageNs"]) * 1e-9
     c = read_counters(dirs)
     import fa_inputs
-    w = fa_inputs.CONFIGS[args.workload]
-    table = kernel_table(w["dtype"], w["B"], w["H"], w["N"], w["d"], w["causal"])
+    if is_fp8(args.workload):
+        w = fa_inputs.FP8_CONFIGS[args.workload]
+        table = {"fwd_fp8_kernel": ("mfma", flops(w["B"], w["H"], w["N"], w["d"], w["causal"])[0], "flop")}
+    else:
+        w = fa_inputs.CONFIGS[args.workload]
+        table = kernel_table(w["dtype"], w["B"], w["H"], w["N"], w["d"], w["causal"])
+    # flops of one MFMA instruction: 32x32x16 bf16, 32x32x64 fp8
+    per_instr = {"fwd_fp8_kernel": 131072.0}
     lines = [f"# MFMA, VALU and LDS use per kernel: {args.workload}", "",
              "Commands (from the repository root, on one MI355X; one `--pmc` run per counter group):", ""]
     for d in dirs:
@@ -232,14 +241,16 @@ def summarize_sq(args):
               "| kernel | ms | clock (GHz) | MFMA instr. / algorithmic | MFMA busy | MFMA busy with VALU co-issue "
               "| other VALU instr. per MFMA (exp included) | exp per MFMA | LDS instr. per MFMA | CU busy |",
               "|---|---|---|---|---|---|---|---|---|---|"]
-    for n in ("fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel"):
+    for n in ("fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"):
         k = c.get(n, {})
         if "GRBM_GUI_ACTIVE" not in k or n not in dur:
             continue
         cyc = k["GRBM_GUI_ACTIVE"] / 8.0
         clock = cyc / dur[n] / 1e9
         mfma = k.get("SQ_INSTS_MFMA", float("nan"))
-        algo = table[n][1] / 32768.0
+        if n not in table:
+            continue
+        algo = table[n][1] / per_instr.get(n, 32768.0)
         busy = k.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (1024.0 * cyc)
         coex = k.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")) / k.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
         valu = (k.get("SQ_INSTS_VALU", float("nan")) - mfma) / mfma
