@@ -12,3 +12,4 @@ from .attention import backward, forward, forward_rows, probabilities, scores  #
 from .online import chunk_merge, tiled_forward  # noqa: F401
 from .softmax import softmax_rows  # noqa: F401
 from .fp8 import decode_e4m3, forward_fp8  # noqa: F401
+from .dropout import backward_dropout, forward_dropout, keep_mask, philox4x32_10  # noqa: F401
