@@ -59,6 +59,12 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp,
                                  ctypes.POINTER(vp)]
     lib.fa_bwd_timed.restype = i
+    u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, u64, u32, vp]
+    lib.fa_fwd_dropout.restype = i
+    lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, u64, u32, vp, sz, vp,
+                                   ctypes.POINTER(vp)]
+    lib.fa_bwd_dropout.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_softmax_rows.argtypes = [vp, vp, vp, ctypes.c_longlong, i, i, vp]
@@ -240,3 +246,62 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, sc
     if st != FA_OK:
         raise FAError(st, "fa_fwd_fp8")
     return o, lse
+
+
+def fa_fwd_dropout(q, k, v, dropout_p, seed, offset=0, o=None, lse=None, scale=None, causal=False, stream=None):
+    """Forward pass with dropout on the probabilities (bf16): returns (o, lse)."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check("o", o, (B, H, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, sc,
+                            1 if causal else 0, _dtype_code(q), float(dropout_p), int(seed), int(offset),
+                            _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_dropout")
+    return o, lse
+
+
+def fa_bwd_dropout(q, k, v, o, lse, do, dropout_p, seed, offset=0, dq=None, dk=None, dv=None, scale=None,
+                   causal=False, workspace=None, stream=None, events=None):
+    """Backward pass of fa_fwd_dropout (same seed and offset): returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    code = _dtype_code(q)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d, code), dtype=torch.uint8, device=dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    handles = None
+    if events is not None:
+        if len(events) != FA_BWD_LAUNCHES + 1:
+            raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        handles = (ctypes.c_void_p * len(events))()
+        for n, ev in enumerate(events):
+            if ev.cuda_event == 0:
+                ev.record(s)
+            handles[n] = ev.cuda_event
+    st = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0, code,
+                            float(dropout_p), int(seed), int(offset), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream_handle(stream, dev), handles)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dropout")
+    return dq, dk, dv

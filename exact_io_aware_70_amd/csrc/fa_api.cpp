@@ -85,6 +85,58 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                       workspace_bytes, stream, events);
 }
 
+// Dropout parameters: p in [0, 1); threshold round(256 p); key from the 64-bit seed.
+static bool make_dropout(float p, unsigned long long seed, unsigned offset, fa::DropoutArgs* d) {
+    if (!(p >= 0.0f && p < 1.0f)) return false;
+    const double t = std::floor(256.0 * (double)p + 0.5);
+    d->k0 = (uint32_t)(seed & 0xffffffffull);
+    d->k1 = (uint32_t)(seed >> 32);
+    d->offset = offset;
+    d->thr = (uint32_t)(t < 0.0 ? 0.0 : (t > 256.0 ? 256.0 : t));
+    d->inv_keep = 1.0f / (1.0f - p);
+    return true;
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, float dropout_p, unsigned long long seed, unsigned offset,
+                   void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    const int st = check_common(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    fa::DropoutArgs dr{};
+    if (dtype != FA_BF16 || !make_dropout(dropout_p, seed, offset, &dr)) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, dtype, dropout_p > 0.0f ? 1 : 0, dr};
+    const hipError_t e = fa::launch_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                   float dropout_p, unsigned long long seed, unsigned offset, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* events) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+    const int st = check_common(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    fa::DropoutArgs dr{};
+    if (dtype != FA_BF16 || !make_dropout(dropout_p, seed, offset, &dr)) return FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype) || !aligned(workspace, 256))
+        return FA_ERR_WORKSPACE;
+    if (events)
+        for (int i = 0; i <= FA_BWD_LAUNCHES; ++i)
+            if (!events[i]) return FA_ERR_NULL;
+    float* delta = static_cast<float*>(workspace);
+    float* lse2 = delta + round_up((size_t)B * H * N * sizeof(float), 256) / sizeof(float);
+    fa::BwdArgs a{q,     k,    v,   o,     dout,  lse,   dq,  dk,    dv,    B,      H,
+                  N,     d,    scale, causal ? 1 : 0, dtype, delta, lse2, events, dropout_p > 0.0f ? 1 : 0, dr};
+    const hipError_t e = fa::launch_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale, const float* k_descale,
                const float* v_descale, void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
                void* stream) {
@@ -116,7 +168,7 @@ const char* fa_status_string(int status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
         case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be >= 1 and the grid must fit in 2^31 - 1 workgroups";
-        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64 or 128, dtype FA_F32 or FA_BF16, scale finite and > 0";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64 or 128, dtype FA_F32 or FA_BF16, scale finite and > 0 (dropout: bf16, 0 <= p < 1; FP8: d = 128)";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned (lse 4-byte)";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a kernel launch";

@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -70,11 +71,14 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
 // the B operands of dV^T += dO^T P and dK^T += Q^T dS without any shuffle.
 // Query rows past N load as zeros with lse = D = 0: their P is 1 but multiplies zero dO
 // rows, and their dS = P (0 - 0) = 0, so they contribute nothing.
-template <int D, int NW, bool CAUSAL>
+// DROP: dropout (dV takes the dropped P; dS = P (Z dP - D) with Z the keep factor; the
+// 1 / (1 - p) of dV is applied at the store).
+template <int D, int NW, bool CAUSAL, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2) {
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2,
+    DropoutArgs drop) {
     constexpr int BQ = 32;              // query rows per sub-tile
     constexpr int NS = 4;               // LDS stages
     constexpr int STAGE = BQ * D;       // bf16 elements per tensor per stage
@@ -165,8 +169,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     // The arithmetic of one query sub-tile whose rows start at stage offset `so` (elements);
     // MASKED applies the causal mask of the wave's own diagonal sub-tile (query rows
     // kw0 .. kw0 + 31: key l32 > query 8(r/4) + 4 half + r%4).
-    auto body = [&](auto masked, int so, int ls) {
+    auto body = [&](auto masked, int so, int ls, int qs0) {
         constexpr bool MASKED = decltype(masked)::value;
+        uint32_t dm[4];
+        if constexpr (DROP) dropout_bytes<false>(drop, (uint32_t)bh, mykey, qs0, lane, dm);
         // S = Q K^T and dP = dO V^T: lane = key, register r = query 8(r/4) + 4 half + r%4.
         f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
@@ -183,10 +189,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
                 float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -l4[e]));
                 if (MASKED && l32 > 8 * g + 4 * half + e) p = 0.f;
                 sacc[4 * g + e] = p;
-                pacc[4 * g + e] = p * (pacc[4 * g + e] - d4[e]);
+                if constexpr (DROP)
+                    pacc[4 * g + e] = p * (pacc[4 * g + e] * dropout_factor(dm, 4 * g + e, drop) - d4[e]);
+                else
+                    pacc[4 * g + e] = p * (pacc[4 * g + e] - d4[e]);
             }
         }
-        const bf16x8 pb[2] = {to_bf16x8(sacc, 0), to_bf16x8(sacc, 8)};
+        bf16x8 pb[2] = {to_bf16x8(sacc, 0), to_bf16x8(sacc, 8)};
+        if constexpr (DROP) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                u32x4 w4 = __builtin_bit_cast(u32x4, pb[cc]);
+                uint32_t w[4] = {w4[0], w4[1], w4[2], w4[3]};
+                dropout_apply_bf16(w, dm[2 * cc], dm[2 * cc + 1], drop.thr);
+                pb[cc] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+        }
         const bf16x8 sb[2] = {to_bf16x8(pacc, 0), to_bf16x8(pacc, 8)};
         // dV^T += dO^T P, dK^T += Q^T dS: for k-step cc the B operands hold queries
         // 16cc + 8(i/4) + 4 half + i%4; the transposed reads fetch rows 16cc + tr_row (+8).
@@ -212,7 +230,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, t_begin + i + NS - 1);
         const int t = t_begin + i;
         if (!wave_live || (CAUSAL ? t <= wave_first : false)) return;
-        body(std::false_type{}, ST * STAGE, ST);
+        body(std::false_type{}, ST * STAGE, ST, t * BQ);
     };
 
     using S0 = std::integral_constant<int, 0>;
@@ -257,7 +275,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             load_lds_b32(rl, lds_addr(&LDs[wave][0][0]), (uint32_t)(lane * 4));
             load_lds_b32(rd, lds_addr(&LDs[wave][1][0]), (uint32_t)(lane * 4));
             wait_vmcnt<0>();
-            body(std::true_type{}, wave * STAGE, wave);
+            body(std::true_type{}, wave * STAGE, wave, kw0);
         }
     }
 
@@ -272,7 +290,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     wk[e] = (__bf16)(dk[db][4 * g + e] * scale);
-                    wv[e] = (__bf16)dv[db][4 * g + e];
+                    wv[e] = (__bf16)(DROP ? dv[db][4 * g + e] * drop.inv_keep : dv[db][4 * g + e]);
                 }
                 const int col = 32 * db + 8 * g + 4 * half;
                 *reinterpret_cast<u32x2*>(dkrow + col) = __builtin_bit_cast(u32x2, wk);
@@ -287,11 +305,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 // NS-stage LDS ring as the forward.  S^T = K Q^T and dP^T = V dO^T put one query per lane,
 // so lse and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T (K^T by transposed
 // reads).  This recomputes S and dP instead of accumulating dQ with atomics.
-template <int D, int NW, bool CAUSAL>
+// DROP: dropout (dS = P (Z dP - D) with Z the keep factor).
+template <int D, int NW, bool CAUSAL, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
-    __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2) {
+    __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, DropoutArgs drop) {
     constexpr int BK = 32, NS = 4, STAGE = BK * D, CPR = D / 8, NT = NW * 64;
     constexpr int BM = 32 * NW, DC = D / 16, DB = D / 32;
     constexpr int LPT = BK * CPR / NT;
@@ -386,8 +405,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
                 if (CAUSAL ? (key > myq) : (key >= N)) s[r] = 0.f;
             }
         }
+        if constexpr (DROP) {
+            uint32_t dm[4];
+            dropout_bytes<true>(drop, (uint32_t)bh, myq, kv0, lane, dm);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
+            for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] * dropout_factor(dm, r, drop) - del);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
+        }
         const bf16x8 sb[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
@@ -612,7 +638,7 @@ hipError_t mark(const BwdArgs& a, int i, hipStream_t st) {
     return a.events ? hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st) : hipSuccess;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
     constexpr int NW = 4;
     hipError_t e;
@@ -620,16 +646,17 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
     if ((e = launch_delta<__bf16, D>(a, st)) != hipSuccess) return e;
     if ((e = mark(a, 1, st)) != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)((long long)nkt * a.B * a.H)), dim3(NW * 64), 0,
-                       st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
-                       (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv, a.N, nkt, a.scale,
-                       a.scale * kLog2e);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL, DROP>), dim3((unsigned)((long long)nkt * a.B * a.H)),
+                       dim3(NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv,
+                       a.N, nkt, a.scale, a.scale * kLog2e, a.drop);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(a, 2, st)) != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)((long long)nqt * a.B * a.H)), dim3(NW * 64), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout,
-                       (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dq, a.N, nqt, a.scale, a.scale * kLog2e);
+    hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL, DROP>), dim3((unsigned)((long long)nqt * a.B * a.H)),
+                       dim3(NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dq, a.N, nqt,
+                       a.scale, a.scale * kLog2e, a.drop);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(a, 3, st);
 }
@@ -658,8 +685,14 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     if (a.dtype == kBF16) {
-        if (a.d == 128) return a.causal ? launch_bwd_bf16<128, true>(a, st) : launch_bwd_bf16<128, false>(a, st);
-        return a.causal ? launch_bwd_bf16<64, true>(a, st) : launch_bwd_bf16<64, false>(a, st);
+        if (a.dropout) {
+            if (a.d == 128)
+                return a.causal ? launch_bwd_bf16<128, true, true>(a, st) : launch_bwd_bf16<128, false, true>(a, st);
+            return a.causal ? launch_bwd_bf16<64, true, true>(a, st) : launch_bwd_bf16<64, false, true>(a, st);
+        }
+        if (a.d == 128)
+            return a.causal ? launch_bwd_bf16<128, true, false>(a, st) : launch_bwd_bf16<128, false, false>(a, st);
+        return a.causal ? launch_bwd_bf16<64, true, false>(a, st) : launch_bwd_bf16<64, false, false>(a, st);
     }
     if (a.d == 128) return a.causal ? launch_bwd_f32<128, true>(a, st) : launch_bwd_f32<128, false>(a, st);
     return a.causal ? launch_bwd_f32<64, true>(a, st) : launch_bwd_f32<64, false>(a, st);

@@ -17,6 +17,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -48,10 +49,12 @@ struct FwdTile {
 
 // Two waves per SIMD: the register budget stays within 256 VGPRs, so every MFMA keeps its
 // accumulator in ordinary VGPRs and the softmax reads the scores in place.
-template <int D, int NW, int QB, bool CAUSAL>
+// DROP: dropout of the probabilities in the P V product (the row sums, hence lse, stay
+// undropped; the 1 / (1 - p) scale is folded into the epilogue).
+template <int D, int NW, int QB, bool CAUSAL, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, DropoutArgs drop) {
     using T = FwdTile<D>;
     constexpr int BK = T::BK, NS = T::NS, CPR = T::CPR, STAGE = T::STAGE;
     constexpr int RW = 32 * QB;         // query rows per wave
@@ -272,7 +275,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         interleave_mfma<DC * QB, 0, 6>();
         pin_regs(pb);  // keep the exponentials in region 1 (they would sink to their use)
         if (needs_mask(i + 1)) mask(i + 1, nxt);
-        pv(cur_st, pb);
+        if constexpr (DROP) {
+            bf16x8 pd[QB][2];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                uint32_t m[4];
+                dropout_bytes<true>(drop, (uint32_t)bh, wq0 + 32 * qb + l32, i * BK, lane, m);
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    u32x4 w4 = __builtin_bit_cast(u32x4, pb[qb][cc]);
+                    uint32_t w[4] = {w4[0], w4[1], w4[2], w4[3]};
+                    dropout_apply_bf16(w, m[2 * cc], m[2 * cc + 1], drop.thr);
+                    pd[qb][cc] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+                }
+            }
+            pv(cur_st, pd);
+        } else {
+            pv(cur_st, pb);
+        }
         rowsum(pb);
         raise_ref(nxt);
     };
@@ -294,7 +314,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         const float l = sum_halves(lsum[qb]);
         const int myq = wq0 + 32 * qb + l32;
         if (myq < N) {
-            const float inv = 1.0f / l;
+            const float inv = (DROP ? drop.inv_keep : 1.0f) / l;
             __bf16* orow = O + base + (size_t)myq * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -432,9 +452,14 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t st) {
     constexpr int BM = 32 * QB * NW;
     const int nqt = (a.N + BM - 1) / BM;
     const long long grid = (long long)nqt * a.B * a.H;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
-                       a.N, nqt, a.scale * kLog2e);
+    if (a.dropout)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+                           (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
+                           a.N, nqt, a.scale * kLog2e, a.drop);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL, false>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+                           (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
+                           a.N, nqt, a.scale * kLog2e, a.drop);
     return hipGetLastError();
 }
 

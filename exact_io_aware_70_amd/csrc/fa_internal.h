@@ -3,11 +3,21 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
+
+// Dropout of the probabilities (see fa_dropout.h): Philox key, counter word 3, 8-bit keep
+// threshold (keep iff byte >= thr) and 1 / (1 - p).
+struct DropoutArgs {
+    uint32_t k0, k1;
+    uint32_t offset;
+    uint32_t thr;
+    float inv_keep;
+};
 
 struct FwdArgs {
     const void* q;
@@ -19,6 +29,8 @@ struct FwdArgs {
     float scale;
     int causal;
     int dtype;
+    int dropout;       // nonzero: apply `drop`
+    DropoutArgs drop;
 };
 
 struct BwdArgs {
@@ -38,6 +50,8 @@ struct BwdArgs {
     float* delta;  // workspace: D_i = rowsum(dout * o), float [B, H, N]
     float* lse2;   // workspace: lse * log2(e), float [B, H, N]
     void* const* events;  // optional: hipEvent_t recorded before each launch and after the last
+    int dropout;          // nonzero: apply `drop`
+    DropoutArgs drop;
 };
 
 struct Fp8FwdArgs {

@@ -112,6 +112,29 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * Forward and backward passes with dropout on the probabilities ("How FlashAttention
+ * Actually Works" -- "Why Attention Is Slow": dropout is one of the steps a fused kernel
+ * runs on chip).  The same arguments and behaviour as fa_fwd / fa_bwd (fa_bwd_timed when
+ * `events` is non-NULL), plus:
+ *   dropout_p in [0, 1) (FA_ERR_UNSUPPORTED otherwise; p = 0 is plain attention);
+ *   seed, offset: the random stream.  Mask of head bh = b * H + h: Philox4x32-10 (Salmon,
+ *     Moraes, Dror, Shaw, SC 2011) with counter (j >> 2, i >> 2, bh, offset) and key (seed
+ *     mod 2^32, seed >> 32); element (query i, key j) reads byte (j & 3) of output word
+ *     (i & 3) and is kept iff that byte >= round(256 dropout_p).
+ * O = (P o Z) V with Z = keep / (1 - p); lse is the logsumexp of the undropped scores.  The
+ * backward pass regenerates the same mask from (seed, offset): dV = (P o Z)^T dout,
+ * dS = P o (Z o (dout V^T) - D).  Pass the forward's seed and offset to the backward.
+ * bf16 only (FA_ERR_UNSUPPORTED for FA_F32).
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, float dropout_p, unsigned long long seed, unsigned offset,
+                   void* stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                   float dropout_p, unsigned long long seed, unsigned offset, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* events);
+
+/*
  * FP8 forward pass: the same tiled online-softmax forward as fa_fwd over OCP E4M3 inputs,
  * with both products on the FP8 matrix cores ("Breaking the Memory Wall" -- "The
  * Solution: IO-Awareness & Tiling", items 1-2; "How does FlashAttention optimize memory

@@ -71,8 +71,11 @@ def keep_mask(bh: int, n_q: int, n_k: int, p: float, seed: int, offset: int) -> 
     return u >= threshold(p)
 
 
-def forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int = 0):
-    """O = (P o Z) V and the undropped lse, per (batch, head); arrays [B, H, N, d]."""
+def forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int = 0, bh0: int = 0):
+    """O = (P o Z) V and the undropped lse, per (batch, head); arrays [B, H, N, d].
+
+    The mask of array head (b, h) is that of head index bh0 + b * H + h (bh0 places a slice
+    of heads inside a larger batch)."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, N, _ = q.shape
     o = np.empty_like(v)
@@ -80,21 +83,22 @@ def forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, of
     for b in range(B):
         for h in range(H):
             pr, m, l = probabilities(q[b, h], k[b, h], scale, causal)
-            z = keep_mask(b * H + h, N, N, p, seed, offset) / (1.0 - p)
+            z = keep_mask(bh0 + b * H + h, N, N, p, seed, offset) / (1.0 - p)
             o[b, h] = (pr * z) @ v[b, h]
             lse[b, h] = m + np.log(l)
     return o, lse
 
 
-def backward_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: int, offset: int = 0):
-    """(dQ, dK, dV) of L = sum(O * dO) for the forward above; arrays [B, H, N, d]."""
+def backward_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: int, offset: int = 0, bh0: int = 0):
+    """(dQ, dK, dV) of L = sum(O * dO) for the forward above; arrays [B, H, N, d] (bh0 as
+    in ``forward_dropout``)."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, H, N, _ = q.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for b in range(B):
         for h in range(H):
             pr, _, _ = probabilities(q[b, h], k[b, h], scale, causal)
-            z = keep_mask(b * H + h, N, N, p, seed, offset) / (1.0 - p)
+            z = keep_mask(bh0 + b * H + h, N, N, p, seed, offset) / (1.0 - p)
             g = do[b, h]
             dv[b, h] = (pr * z).T @ g
             dp = z * (g @ v[b, h].T)

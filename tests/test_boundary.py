@@ -34,7 +34,7 @@ def test_header_is_plain_c():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_fp8", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string",
+    assert {"fa_fwd", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string",
             "fa_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
@@ -195,3 +195,18 @@ def test_fp8_bad_sizes(kw, code):
 @pytest.mark.parametrize("which,off", [("q", 8), ("o", 4), ("lse", 2), ("qd", 2)])
 def test_fp8_misaligned(which, off):
     assert call_fp8(ptrs={which: P + off}) == -4
+
+
+def test_dropout_rejects_bad_arguments():
+    lib = fa.load_library()
+    a = GOOD
+    def fwd(p=0.1, dtype=1, q=P):
+        return lib.fa_fwd_dropout(q, P, P, P, P, a["B"], a["H"], a["N"], a["d"], a["scale"], 0, dtype, p, 1, 0, None)
+    def bwd(p=0.1, dtype=1, ws=P, events=None):
+        return lib.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["N"], a["d"], a["scale"], 0, dtype, p,
+                                  1, 0, ws, 1 << 30, None, events)
+    assert fwd(q=None) == -1
+    assert fwd(p=1.0) == -3 and fwd(p=-0.1) == -3 and fwd(p=float("nan")) == -3 and fwd(dtype=0) == -3
+    assert bwd(p=1.5) == -3 and bwd(dtype=0) == -3 and bwd(ws=None) == -5
+    events = (ctypes.c_void_p * 4)(P, P, None, P)
+    assert bwd(events=events) == -1

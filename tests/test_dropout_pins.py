@@ -158,3 +158,15 @@ def test_planted_mistakes_are_caught(mistake):
         except AssertionError:
             caught += 1
     assert (caught > 0) == (mistake is not None), (mistake, caught)
+
+
+def test_head_offset_places_a_slice():
+    """A slice of heads with bh0 gives the same result as the full batch."""
+    q, k, v, do = _case(seed=14, N=10)
+    full = oracle.forward_dropout(q, k, v, 0.4, True, 0.3, 9, 2)[0]
+    part = oracle.forward_dropout(q[:, 1:2], k[:, 1:2], v[:, 1:2], 0.4, True, 0.3, 9, 2, bh0=1)[0]
+    np.testing.assert_array_equal(full[:, 1:2], part)
+    g_full = oracle.backward_dropout(q, k, v, do, 0.4, True, 0.3, 9, 2)
+    g_part = oracle.backward_dropout(q[:, 1:2], k[:, 1:2], v[:, 1:2], do[:, 1:2], 0.4, True, 0.3, 9, 2, bh0=1)
+    for a, b in zip(g_full, g_part):
+        np.testing.assert_array_equal(a[:, 1:2], b)

@@ -1,0 +1,96 @@
+"""GPU parity of fa_fwd_dropout / fa_bwd_dropout against the fp64 dropout oracle (the same
+Philox4x32-10 mask regenerated on the CPU), through the C ABI.
+
+Bound per element: 2e-2 + 2^-7 cond (the first-order rounding of the bf16 factor of each
+product, of D taken from the bf16-stored O, and of the bf16 output:
+``gpu_util.dropout_conditions``); mean-abs <= 2e-3 + 2^-8 mean(cond).  With dropout the
+outputs grow by 1 / (1 - p), so the fixed bounds alone would not be fair bf16 bounds.  p = 0 through these entry points must equal the plain path bit for bit."""
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+from tests.gpu_util import assert_parity, dropout_conditions, gpu_available, log, to_device, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def run(case, causal, p, seed, offset):
+    import torch
+    import exact_io_aware_70_amd as fa
+    q, k, v, do = (to_device(case, n) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_dropout(q, k, v, p, seed, offset, scale=case["scale"], causal=causal)
+    dq, dk, dv = fa.fa_bwd_dropout(q, k, v, o, lse, do, p, seed, offset, scale=case["scale"], causal=causal)
+    torch.cuda.synchronize()
+    return [to_f64(t) for t in (o, lse, dq, dk, dv)]
+
+
+def check(case, causal, p, seed, offset, heads, label):
+    o, lse, dq, dk, dv = run(case, causal, p, seed, offset)
+    B, H = case["shape"][:2]
+    vals = {n: case[n]["values"] for n in ("q", "k", "v", "do")}
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        args = [vals[n][sl] for n in ("q", "k", "v")]
+        ref_o, ref_lse = oracle.forward_dropout(*args, case["scale"], causal, p, seed, offset, bh0=b * H + h)
+        ref = oracle.backward_dropout(*args, vals["do"][sl], case["scale"], causal, p, seed, offset, bh0=b * H + h)
+        conds = dropout_conditions(*(vals[n][b, h] for n in ("q", "k", "v", "do")), case["scale"], causal, p,
+                                   seed, offset, b * H + h)
+        log(f"  {label} head ({b},{h})")
+        assert_parity("O", o[sl], ref_o, "bf16", cond=conds[0][None, None], mean_cond=True)
+        assert_parity("lse", lse[sl], ref_lse, "bf16")
+        for nm, got, r, c in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref, conds[1:]):
+            assert_parity(nm, got[sl], r, "bf16", cond=c[None, None], mean_cond=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 300])
+def test_dropout_small(d, causal, N):
+    case = fa_inputs.make_case(2, 2, N, d, "bf16", seed=900 + N + d, with_grad=True)
+    log(f"[dropout] N={N} d={d} causal={causal}")
+    check(case, causal, 0.25, seed=0x1234_5678_9ABC, offset=3, heads=[(0, 0), (0, 1), (1, 0), (1, 1)],
+          label=f"N={N}")
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_dropout_rates(p):
+    case = fa_inputs.make_case(1, 3, 260, 128, "bf16", seed=950, with_grad=True)
+    log(f"[dropout] p={p}")
+    check(case, True, p, seed=77, offset=11, heads=[(0, 0), (0, 2)], label=f"p={p}")
+
+
+def test_dropout_zero_equals_plain():
+    import torch
+    import exact_io_aware_70_amd as fa
+    case = fa_inputs.make_case(2, 2, 333, 128, "bf16", seed=951, with_grad=True)
+    q, k, v, do = (to_device(case, n) for n in ("q", "k", "v", "do"))
+    o0, l0 = fa.fa_fwd(q, k, v, causal=True)
+    o1, l1 = fa.fa_fwd_dropout(q, k, v, 0.0, 123, 0, causal=True)
+    g0 = fa.fa_bwd(q, k, v, o0, l0, do, causal=True)
+    g1 = fa.fa_bwd_dropout(q, k, v, o1, l1, do, 0.0, 123, 0, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert all(torch.equal(a, b) for a, b in zip(g0, g1))
+
+
+def test_dropout_stream_changes_with_seed_and_offset():
+    """Different (seed, offset) give different masks; the same ones reproduce exactly."""
+    import torch
+    import exact_io_aware_70_amd as fa
+    case = fa_inputs.make_case(1, 2, 256, 64, "bf16", seed=952, with_grad=True)
+    q, k, v = (to_device(case, n) for n in ("q", "k", "v"))
+    a, _ = fa.fa_fwd_dropout(q, k, v, 0.3, 5, 0)
+    b, _ = fa.fa_fwd_dropout(q, k, v, 0.3, 5, 0)
+    c, _ = fa.fa_fwd_dropout(q, k, v, 0.3, 6, 0)
+    e, _ = fa.fa_fwd_dropout(q, k, v, 0.3, 5, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and not torch.equal(a, c) and not torch.equal(a, e)
+
+
+def test_dropout_medium_config():
+    """B=2 H=8 N=2048 d=128 causal, p = 0.1: every output of 3 heads against the oracle."""
+    case = fa_inputs.make_case(2, 8, 2048, 128, "bf16", seed=953, with_grad=True)
+    log("[dropout] B=2 H=8 N=2048 d=128 causal p=0.1")
+    check(case, True, 0.1, seed=2024, offset=0, heads=[(0, 0), (1, 3), (1, 7)], label="n2048")
