@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --workload softmax_bf16_r65536_c8192   (the row-softmax kernel on its own)
     python bench.py --workload fwd_fp8_causal_b4h32_n8192_d128   (the E4M3 forward)
+    python bench.py --dropout 0.1   (the same step with dropout on the probabilities)
     python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--copy-mib M] [--workload NAME]
     python bench.py --summarize-sq STATS_CSV PMC_DIR [PMC_DIR ...] [--workload NAME]
 
@@ -56,6 +57,9 @@ def parse():
     p.add_argument("--workload", default="fwd_bf16_causal_b4h32_n8192_d128")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=16, help="heads of the workload the CPU oracle runs")
+    p.add_argument("--dropout", type=float, default=0.0,
+                   help="attention workloads: dropout probability of the probabilities (fa_fwd_dropout / "
+                        "fa_bwd_dropout, seed 1234, offset 0); 0 runs the plain path")
     p.add_argument("--cpu-rows", type=int, default=65536,
                    help="rows of a row-softmax workload the CPU oracle runs")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -547,12 +551,19 @@ def main():
     kinds = kernel_table(case["dtype"], B, H, N, d, causal)
     knames = list(kinds)
 
+    drop = args.dropout
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
-        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=sc, causal=causal, workspace=ws, stream=stream,
-                  events=None if ev is None else ev[1:])
+        if drop > 0.0:
+            fa.fa_fwd_dropout(q, k, v, drop, 1234, 0, o, lse, scale=sc, causal=causal, stream=stream)
+            fa.fa_bwd_dropout(q, k, v, o, lse, do, drop, 1234, 0, dq, dk, dv, scale=sc, causal=causal, workspace=ws,
+                              stream=stream, events=None if ev is None else ev[1:])
+        else:
+            fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
+            fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=sc, causal=causal, workspace=ws, stream=stream,
+                      events=None if ev is None else ev[1:])
 
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20)
@@ -589,7 +600,7 @@ def main():
     bwd_ms = sum(avg[n] for n in knames[1:])
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if case["dtype"] == "bf16" else PEAK_F32_TFLOPS
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(args.workload) if drop == 0.0 else None  # counters cover the plain kernels
 
     kernels = {}
     for name in knames:
@@ -622,7 +633,7 @@ def main():
         "dtype": case["dtype"],
         "data": "synthetic (seeded N(0,1) Q/K/V/dO, Q x%g)" % cfg["q_scale"],
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
-                   "pass": "fwd+bwd", "step_flops": ff + fb},
+                   "pass": "fwd+bwd", "step_flops": ff + fb, **({"dropout_p": drop} if drop > 0.0 else {})},
         "pct_peak": round(100 * value / peak, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
                 "pct_peak": round(100 * ff / (fwd_ms * 1e-3) / 1e12 / peak, 2), "flops": ff},
