@@ -44,7 +44,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
 KERNEL_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd.hip", "exact_io_aware_70_amd/csrc/fa_bwd.hip",
-                  "exact_io_aware_70_amd/csrc/fa_device.h"]
+                  "exact_io_aware_70_amd/csrc/fa_device.h", "exact_io_aware_70_amd/csrc/fa_dropout.h"]
 SOFTMAX_SOURCES = ["exact_io_aware_70_amd/csrc/fa_softmax.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
 FP8_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
 

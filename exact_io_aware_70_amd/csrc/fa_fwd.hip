@@ -33,8 +33,8 @@ constexpr float kRescaleSlack = 8.0f;
 // Workgroup: NW waves, each owning QB blocks of 32 query rows (every K/V operand read from
 // LDS feeds QB MFMAs).  K/V stream in sub-tiles of 32 keys through an NS-stage
 // LDS ring filled by buffer loads that write LDS directly (no register staging).  Rows of
-// a stage are stored with their 16-byte chunks XOR-swizzled by (row % 8), which keeps both
-// the row-wise K reads and the transposed V reads free of bank conflicts.
+// a stage are stored with their 16-byte chunks XOR-swizzled by swz_row(row) (fa_device.h),
+// which keeps both the row-wise K reads and the transposed V reads free of bank conflicts.
 //
 // Software pipeline per sub-tile i (one barrier each):
 //   exponentials of S(i) on the VALU  ||  S(i+1) = K(i+1) Q^T on the MFMA
