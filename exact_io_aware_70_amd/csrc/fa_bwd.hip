@@ -306,8 +306,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 // so lse and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T (K^T by transposed
 // reads).  This recomputes S and dP instead of accumulating dQ with atomics.
 // DROP: dropout (dS = P (Z dP - D) with Z the keep factor).
+// Occupancy: two waves per SIMD at d = 128; three at d = 64, where the kernel fits 168 VGPRs.
 template <int D, int NW, bool CAUSAL, bool DROP>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
+                               amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2))) void dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, DropoutArgs drop) {

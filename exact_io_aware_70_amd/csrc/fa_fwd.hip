@@ -47,12 +47,18 @@ struct FwdTile {
     static constexpr int STAGE = BK * D;   // bf16 elements per tensor per stage
 };
 
-// Two waves per SIMD: the register budget stays within 256 VGPRs, so every MFMA keeps its
-// accumulator in ordinary VGPRs and the softmax reads the scores in place.
+// Two waves per SIMD at d = 128: the register budget stays within 256 VGPRs, so every MFMA
+// keeps its accumulator in ordinary VGPRs and the softmax reads the scores in place.  At
+// d = 64 the kernel needs under 128 VGPRs and a 32 KiB ring, so four waves per SIMD (three
+// with dropout, whose mask needs more registers) hide more latency.
 // DROP: dropout of the probabilities in the P V product (the row sums, hence lse, stay
 // undropped; the 1 / (1 - p) scale is folded into the epilogue).
+template <int D, bool DROP>
+struct FwdWaves : std::integral_constant<int, D == 64 ? (DROP ? 3 : 4) : 2> {};
+
 template <int D, int NW, int QB, bool CAUSAL, bool DROP>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
+                               amdgpu_waves_per_eu(FwdWaves<D, DROP>::value, FwdWaves<D, DROP>::value))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, DropoutArgs drop) {
     using T = FwdTile<D>;
