@@ -98,6 +98,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
+    // One head at a time: the workgroups in flight share one head's Q / dO stream in L2
+    // (pairs of heads, as in the forward, made this kernel 16-24% slower at N >= 8192).
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = L / nkt;
     const int kt = L % nkt;              // causal: low key tiles see the most queries
@@ -326,8 +328,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nqt;
-    const int q0 = (nqt - 1 - (L % nqt)) * BM;  // heaviest (causal) tiles first
+    int bh, rank;
+    tile_order(L, nqt, gridDim.x / nqt, bh, rank);
+    const int q0 = (nqt - 1 - rank) * BM;  // heaviest (causal) tiles first
     const size_t base = (size_t)bh * N * D;
     const int wq0 = q0 + 32 * wave, myq = wq0 + l32;
 

@@ -83,8 +83,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
     const int half = lane >> 5, l32 = lane & 31;
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nqt;
-    const int qt = nqt - 1 - (L % nqt);  // heaviest (causal) tiles first
+    int bh, rank;
+    tile_order(L, nqt, gridDim.x / nqt, bh, rank);
+    const int qt = nqt - 1 - rank;  // heaviest (causal) tiles first
     const int q0 = qt * BM;
     const size_t base = (size_t)bh * N * D;
     const int wq0 = q0 + wave * 32;
