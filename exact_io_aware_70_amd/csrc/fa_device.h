@@ -191,14 +191,22 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
     return (g % 8 == 0) ? (b % 8) * (g / 8) + b / 8 : b;
 }
 
-// Work order over a grid of nheads x ntiles workgroups (logical id L, after xcd_remap): heads
-// go in pairs, and within a pair the two heads' tiles alternate, rank 0 (the heaviest causal
-// tile) first.  Taking one head at a time can leave the last head's heaviest tiles starting
-// after nearly everything else: a list-scheduling model of 64 slots per XCD puts the loss
-// near 20% for 8 heads of 32 tiles per XCD.  Two heads side by side remove that tail, while
-// the workgroups in flight still share few heads' K/V in L2.  An odd head count leaves the
-// last head on its own.
+// Work order over a grid of nheads x ntiles workgroups (logical id L, after xcd_remap); rank
+// 0 is a head's heaviest causal tile.  By default one head at a time, heaviest tile first:
+// the workgroups in flight on an XCD then share one head's K/V stream in L2.  With fewer than
+// kPairTilesBelow tiles per head, that order can leave the last head's heaviest tiles starting
+// after nearly everything else (a list-scheduling model of 64 slots per XCD loses up to a
+// third at 32 tiles per head and nothing at 64 or 128).  Heads then go in pairs whose tiles
+// alternate, which removes the tail; it costs L2 reuse (at N = 8192 it raised the forward's
+// HBM bytes from 1.14x to 1.52x the compulsory ones), so it is kept to the short case.  An odd
+// head count leaves the last head on its own.
+constexpr int kPairTilesBelow = 64;
 __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& head, int& rank) {
+    if (ntiles >= kPairTilesBelow) {
+        head = L / ntiles;
+        rank = L - head * ntiles;
+        return;
+    }
     const int pair = L / (2 * ntiles), j = L - pair * 2 * ntiles;
     if (2 * pair + 1 < nheads) {
         head = 2 * pair + (j & 1);
