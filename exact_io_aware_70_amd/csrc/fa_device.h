@@ -191,10 +191,10 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
     return (g % 8 == 0) ? (b % 8) * (g / 8) + b / 8 : b;
 }
 
-// Work order over a grid of nheads x ntiles workgroups (logical id L, after xcd_remap); rank
-// 0 is a head's heaviest causal tile.  By default one head at a time, heaviest tile first:
-// the workgroups in flight on an XCD then share one head's K/V stream in L2.  With fewer than
-// kPairTilesBelow tiles per head, that order can leave the last head's heaviest tiles starting
+// Work order over a grid of nheads x ntiles workgroups (logical id L, after xcd_remap); rank 0
+// is a head's heaviest causal tile.  By default one head at a time, heaviest tile first: the
+// workgroups in flight on an XCD then share one head's K/V (or Q/dO) stream in L2.  With fewer
+// than kPairTilesBelow tiles per head, that order can leave the last head's heaviest tiles starting
 // after nearly everything else (a list-scheduling model of 64 slots per XCD loses up to a
 // third at 32 tiles per head and nothing at 64 or 128).  Heads then go in pairs whose tiles
 // alternate, which removes the tail; it costs L2 reuse (at N = 8192 it raised the forward's
