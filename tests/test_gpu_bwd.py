@@ -37,6 +37,20 @@ def test_bwd_small(dtype, d, causal, N):
         assert_parity(name, to_f64(got), r, dtype)
 
 
+@pytest.mark.parametrize("B,H", [(1, 3), (1, 5)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_odd_head_counts(B, H, causal):
+    """Odd head counts with several key and query tiles per head (paired-head work order,
+    the last head on its own)."""
+    log(f"[bwd] odd heads B={B} H={H} causal={causal}")
+    case = fa_inputs.make_case(B, H, 700, 128, "bf16", seed=400 + 10 * B + H, with_grad=True)
+    dq, dk, dv = run_bwd(case, causal)
+    ref = oracle.backward(case["q"]["values"], case["k"]["values"], case["v"]["values"], case["do"]["values"],
+                          case["scale"], causal)
+    for name, got, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert_parity(name, to_f64(got), r, "bf16")
+
+
 def test_bwd_medium_bf16_causal():
     log("[bwd] bf16 causal d=128 N=1000, 2x3 heads")
     case = fa_inputs.make_case(2, 3, 1000, 128, "bf16", seed=301, with_grad=True)

@@ -64,6 +64,16 @@ def test_fp8_small(causal, N):
             check_head(case, causal, b, h, o[b, h], lse[b, h], label=f"N={N}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_odd_head_count(causal):
+    """Five heads of several query tiles each: paired-head work order, last head alone."""
+    case = fa_inputs.make_fp8_case(1, 5, 700, 128, seed=750, q_scale=2.0)
+    log(f"[fp8] odd heads H=5 N=700 causal={causal}")
+    o, lse = run(case, causal)
+    for h in range(5):
+        check_head(case, causal, 0, h, o[0, h], lse[0, h], label=f"H=5 h={h}")
+
+
 def test_fp8_config_b4h8_n2048():
     c = fa_inputs.FP8_CONFIGS["fwd_fp8_b4h8_n2048_d128"]
     case = fa_inputs.make_fp8_case(c["B"], c["H"], c["N"], c["d"], c["seed"], c["q_scale"])

@@ -41,6 +41,15 @@ def test_fwd_small(dtype, d, causal, N):
     check_full(case, causal, f"small {dtype} d={d} causal={causal} N={N}")
 
 
+@pytest.mark.parametrize("B,H", [(1, 3), (1, 5), (3, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_odd_head_counts(B, H, causal):
+    """Odd head counts with several query tiles per head: the workgroup order pairs heads
+    when a head has few tiles, and an odd count leaves the last head on its own."""
+    case = fa_inputs.make_case(B, H, 700, 128, "bf16", seed=300 + 10 * B + H)
+    check_full(case, causal, f"bf16 B={B} H={H} N=700 causal={causal}")
+
+
 def test_fwd_large_logits_bf16():
     """Q drawn x3 (logits std ~3) with a long causal row: the online rescale is exercised."""
     case = fa_inputs.make_case(1, 4, 2000, 128, "bf16", seed=77, q_scale=3.0)
