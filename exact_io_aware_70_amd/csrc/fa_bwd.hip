@@ -128,6 +128,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 
     const int t_begin = CAUSAL ? k0 / BQ : 0;   // first query sub-tile any key here can see
     const int nsteps = (N + BQ - 1) / BQ - t_begin;
+    // The ring walks the query sub-tiles from the last one down to t_begin, so the workgroups
+    // of a head, which all start at the last sub-tile, read the same Q / dO sub-tile at about
+    // the same time and an XCD fetches it from HBM about once.  Walking up from each one's own
+    // diagonal, they read different sub-tiles at a time and rely on L2 holding the head's whole
+    // Q / dO: at B=4 H=32 N=8192 that fetched 1.42x the compulsory bytes, against 1.19x now.
+    const int t_last = t_begin + nsteps - 1;
+    auto tile_of = [&](int i) { return i < nsteps ? t_last - i : -1; };  // -1: past the end
     const int wave_first = CAUSAL ? kw0 / BQ : 0;
     const bool wave_live = kw0 < N;
 
@@ -141,7 +148,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     // wave writes the (identical) lse / D rows, so each wave issues the same loads.
     auto issue = [&](auto st, int t) {
         constexpr int ST = decltype(st)::value;
-        const int q0 = t * BQ;
+        const int q0 = t < 0 ? N : t * BQ;  // past the end: zero rows, the loads read zeros
         const uint32_t rows = (uint32_t)max(0, N - q0);
         const i32x4 rq = make_rsrc(Q + base + (size_t)min(q0, N) * D, rows * D * 2);
         const i32x4 ro = make_rsrc(dO + base + (size_t)min(q0, N) * D, rows * D * 2);
@@ -231,8 +238,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         constexpr int ST = decltype(st)::value;
         wait_vmcnt<(NS - 2) * LPS>();  // sub-tile i has landed (this wave's share) ...
         __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
-        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, t_begin + i + NS - 1);
-        const int t = t_begin + i;
+        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, tile_of(i + NS - 1));
+        const int t = tile_of(i);
         if (!wave_live || (CAUSAL ? t <= wave_first : false)) return;
         body(std::false_type{}, ST * STAGE, ST, t * BQ);
     };
@@ -242,9 +249,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
     static_assert(NS == 4, "the loop below is unrolled over four stages");
-    issue(S0{}, t_begin);
-    issue(S1{}, t_begin + 1);
-    issue(S2{}, t_begin + 2);
+    issue(S0{}, tile_of(0));
+    issue(S1{}, tile_of(1));
+    issue(S2{}, tile_of(2));
     int i = 0;
     for (; i + 3 < nsteps; i += 4) {
         step(S0{}, i);
