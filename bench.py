@@ -273,15 +273,34 @@ def summarize_sq(args):
     print("\n".join(lines))
 
 
+def host_info():
+    """Threads the oracle's BLAS uses, and what the host is: CPU model and BLAS library."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, cores = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            cores = max(i.get("num_threads", 1) for i in pools)
+            blas = ", ".join(f"{i.get('internal_api', '?')} {i.get('version', '?')}" for i in pools)
+    except Exception:
+        pass
+    return cores, {"cpu_model": model, "blas": blas}
+
+
 def cpu_baseline(case, causal, heads):
     """The fp64 oracle (as it stands) on `heads` heads of the workload: forward + backward."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores, host = host_info()
     B0, H0 = case["shape"][:2]
     heads = min(heads, B0 * H0)
     sel = [(b, h) for b in range(B0) for h in range(H0)][:heads]
@@ -295,10 +314,12 @@ def cpu_baseline(case, causal, heads):
         t_total += time.perf_counter() - t0
     _, _, N, d = case["shape"]
     ff, fb = flops(1, heads, N, d, causal)
+    # The oracle materialises all of S and P: 2 + 5 products of 2 N^2 d flops per head, causal or not.
+    executed = 14.0 * heads * N * N * d
     return {"value": round((ff + fb) / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} of {B0 * H0} heads, full N={N}, d={d}: fp64 forward + backward with explicit S and P "
                       f"({t_total:.1f} s); same flop formula as value",
-            "seconds": round(t_total, 3)}
+            "seconds": round(t_total, 3), "executed_tflops": round(executed / t_total / 1e12, 6), **host}
 
 
 def softmax_bytes(rows, cols, dtype):
@@ -309,11 +330,7 @@ def softmax_bytes(rows, cols, dtype):
 def cpu_softmax_baseline(case, rows):
     """The fp64 oracle (as it stands) on the first `rows` rows of the workload."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores, host = host_info()
     R, C = case["shape"]
     rows = min(rows, R)
     x = case["values"][:rows]
@@ -322,17 +339,13 @@ def cpu_softmax_baseline(case, rows):
     t = time.perf_counter() - t0
     return {"value": round(softmax_bytes(rows, C, case["dtype"]) / t / 1e9, 4), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle", "sample": f"{rows} of {R} rows, cols={C}: fp64 softmax and logsumexp ({t:.1f} s); "
-                                        f"same byte formula as value", "seconds": round(t, 3)}
+                                        f"same byte formula as value", "seconds": round(t, 3), **host}
 
 
 def cpu_fp8_baseline(case, causal, heads):
     """The fp64 FP8 oracle (as it stands) on `heads` heads of the workload: decode + forward."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    cores, host = host_info()
     B0, H0, N, d = case["shape"]
     heads = min(heads, B0 * H0)
     sel = [(b, h) for b in range(B0) for h in range(H0)][:heads]
@@ -344,9 +357,11 @@ def cpu_fp8_baseline(case, causal, heads):
         oracle.forward_fp8(*args, case["scale"], causal)
         t += time.perf_counter() - t0
     ff, _ = flops(1, heads, N, d, causal)
+    executed = 4.0 * heads * N * N * d  # the oracle computes all of S and P
     return {"value": round(ff / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} of {B0 * H0} heads, full N={N}, d={d}: fp64 decode + forward with explicit S and P "
-                      f"({t:.1f} s); same flop formula as value", "seconds": round(t, 3)}
+                      f"({t:.1f} s); same flop formula as value", "seconds": round(t, 3),
+            "executed_tflops": round(executed / t / 1e12, 6), **host}
 
 
 def bench_fp8(args):
