@@ -49,12 +49,15 @@ SOFTMAX_SOURCES = ["exact_io_aware_70_amd/csrc/fa_softmax.hip", "exact_io_aware_
 FP8_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
 
 
+DEFAULT_WORKLOAD = "fwd_bf16_causal_b4h32_n8192_d128"
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="fwd_bf16_causal_b4h32_n8192_d128")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=16, help="heads of the workload the CPU oracle runs")
     p.add_argument("--dropout", type=float, default=0.0,
@@ -208,6 +211,19 @@ def read_counters(dirs):
     return out
 
 
+def counter_names(d):
+    """Counter names of one rocprofv3 --pmc output folder, in first-seen order."""
+    seen = []
+    for dp, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(dp, fn)) as f:
+                    for r in csv.DictReader(f):
+                        if r["Counter_Name"] not in seen:
+                            seen.append(r["Counter_Name"])
+    return seen
+
+
 def summarize_sq(args):
     """MFMA, VALU and LDS use per kernel from SQ counters, as a short markdown table.
 
@@ -234,10 +250,14 @@ def summarize_sq(args):
         table = kernel_table(w["dtype"], w["B"], w["H"], w["N"], w["d"], w["causal"])
     # flops of one MFMA instruction: 32x32x16 bf16, 32x32x64 fp8
     per_instr = {"fwd_fp8_kernel": 131072.0}
+    trace_dir = os.path.dirname(stats_csv)
+    wl = "" if args.workload == DEFAULT_WORKLOAD else f" --workload {args.workload}"
     lines = [f"# MFMA, VALU and LDS use per kernel: {args.workload}", "",
-             "Commands (from the repository root, on one MI355X; one `--pmc` run per counter group):", ""]
+             "Commands (from the repository root, on one MI355X; the kernel-trace statistics come from",
+             f"`rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o run -f csv -- python3 bench.py --steps 5 "
+             f"--warmup 1 --no-cpu-baseline{wl}`; one `--pmc` run per counter group):", ""]
     for d in dirs:
-        lines.append(f"    rocprofv3 --pmc <counters of {os.path.basename(d.rstrip('/'))}> -d {d} -- "
+        lines.append(f"    rocprofv3 --pmc {' '.join(counter_names(d)) or '<none found>'} -d {d} -- "
                      f"python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --workload {args.workload}")
     lines += [f"    python3 bench.py --summarize-sq {stats_csv} {' '.join(dirs)} --workload {args.workload}", "",
               "Counter values are means per dispatch (one warm-up and one timed step).  Durations come from "

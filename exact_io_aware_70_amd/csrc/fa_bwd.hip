@@ -100,11 +100,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     const int half = lane >> 5, l32 = lane & 31;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     int bh, kt;                          // causal: low key tiles see the most queries
-    tile_order(L, nkt, gridDim.x / nkt, bh, kt);
-    // Uniform values: keeping them in SGPRs matters here, at 254 of 256 VGPRs (without it the
-    // causal d = 128 kernel spilled 12 bytes and ran 16-30% slower).
-    bh = __builtin_amdgcn_readfirstlane(bh);
-    kt = __builtin_amdgcn_readfirstlane(kt);
+    tile_order(L, nkt, gridDim.x / nkt, bh, kt);  // scalar results: this kernel has no VGPR to spare
     const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wave, mykey = kw0 + l32;
     const size_t base = (size_t)bh * N * D, rbase = (size_t)bh * N;
 

@@ -200,21 +200,27 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 // alternate, which removes the tail; it costs L2 reuse (at N = 8192 it raised the forward's
 // HBM bytes from 1.14x to 1.52x the compulsory ones), so it is kept to the short case.  An odd
 // head count leaves the last head on its own.
+// Both results are uniform and returned through readfirstlane: the integer divisions are
+// expanded on the VALU, and left in VGPRs they turned every address derived from the head
+// into VALU work inside the loops (and cost the 254-VGPR dK/dV kernel a spill).
 constexpr int kPairTilesBelow = 64;
 __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& head, int& rank) {
+    int h, r;
     if (ntiles >= kPairTilesBelow) {
-        head = L / ntiles;
-        rank = L - head * ntiles;
-        return;
-    }
-    const int pair = L / (2 * ntiles), j = L - pair * 2 * ntiles;
-    if (2 * pair + 1 < nheads) {
-        head = 2 * pair + (j & 1);
-        rank = j >> 1;
+        h = L / ntiles;
+        r = L - h * ntiles;
     } else {
-        head = 2 * pair;
-        rank = j;
+        const int pair = L / (2 * ntiles), j = L - pair * 2 * ntiles;
+        if (2 * pair + 1 < nheads) {
+            h = 2 * pair + (j & 1);
+            r = j >> 1;
+        } else {
+            h = 2 * pair;
+            r = j;
+        }
     }
+    head = __builtin_amdgcn_readfirstlane(h);
+    rank = __builtin_amdgcn_readfirstlane(r);
 }
 
 }  // namespace fa
