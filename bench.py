@@ -261,7 +261,12 @@ def summarize_sq(args):
                      f"python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --workload {args.workload}")
     lines += [f"    python3 bench.py --summarize-sq {stats_csv} {' '.join(dirs)} --workload {args.workload}", "",
               "Counter values are means per dispatch (one warm-up and one timed step).  Durations come from "
-              "the kernel-trace statistics named above.", "",
+              "the kernel-trace statistics named above.", ""]
+    if is_fp8(args.workload):
+        lines += ["The FP8 kernel issues 9 MFMAs per 8 of the attention products (the ninth, with an all-ones "
+                  "operand, sums the rounded probabilities), hence about 1.13 MFMA instructions per algorithmic one.",
+                  ""]
+    lines += [
               "| kernel | ms | clock (GHz) | MFMA instr. / algorithmic | MFMA busy | MFMA busy with VALU co-issue "
               "| other VALU instr. per MFMA (exp included) | exp per MFMA | LDS instr. per MFMA | CU busy |",
               "|---|---|---|---|---|---|---|---|---|---|"]
