@@ -174,9 +174,9 @@ def summarize_pmc(args):
                           "dispatches": len(fv)}
     data = {"workload": args.workload, "source_sha256": sources_digest(args.workload),
             "fetch_scale": ff, "write_scale": fw, "copy_mib": args.copy_mib,
-            "commands": [f"rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -- python3 bench.py --steps 1 --warmup 1 "
+            "commands": [f"rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -f csv -- python3 bench.py --steps 1 --warmup 1 "
                          f"--no-cpu-baseline --copy-mib {args.copy_mib} --workload {args.workload}",
-                         f"rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -- python3 bench.py --steps 1 --warmup 1 "
+                         f"rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -f csv -- python3 bench.py --steps 1 --warmup 1 "
                          f"--no-cpu-baseline --copy-mib {args.copy_mib} --workload {args.workload}",
                          f"python3 bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR> --copy-mib {args.copy_mib} "
                          f"--workload {args.workload}"],
@@ -257,7 +257,7 @@ def summarize_sq(args):
              f"`rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o run -f csv -- python3 bench.py --steps 5 "
              f"--warmup 1 --no-cpu-baseline{wl}`; one `--pmc` run per counter group):", ""]
     for d in dirs:
-        lines.append(f"    rocprofv3 --pmc {' '.join(counter_names(d)) or '<none found>'} -d {d} -- "
+        lines.append(f"    rocprofv3 --pmc {' '.join(counter_names(d)) or '<none found>'} -d {d} -f csv -- "
                      f"python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --workload {args.workload}")
     lines += [f"    python3 bench.py --summarize-sq {stats_csv} {' '.join(dirs)} --workload {args.workload}", "",
               "Counter values are means per dispatch (one warm-up and one timed step).  Durations come from "

@@ -311,12 +311,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 // accumulator in registers); K/V sub-tiles of 32 keys stream through the same swizzled
 // NS-stage LDS ring as the forward.  S^T = K Q^T and dP^T = V dO^T put one query per lane,
 // so lse and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T (K^T by transposed
-// reads).  This recomputes S and dP instead of accumulating dQ with atomics.
+// reads).  This recomputes S and dP instead of accumulating dQ with atomics.  Software
+// pipeline: the exponentials and dS of sub-tile i run on the VALU while the MFMAs compute
+// S and dP of sub-tile i + 1 (two independent chains), then dQ += K(i)^T dS(i).
 // DROP: dropout (dS = P (Z dP - D) with Z the keep factor).
-// Occupancy: two waves per SIMD at d = 128; three at d = 64, where the kernel fits 168 VGPRs.
+// Occupancy: two waves per SIMD at d = 128; three at d = 64, where the kernel fits 168 VGPRs
+// (two with dropout, whose mask would spill at that budget).
+template <int D, bool DROP>
+struct DqWaves : std::integral_constant<int, D == 64 && !DROP ? 3 : 2> {};
+
 template <int D, int NW, bool CAUSAL, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
-                               amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2))) void dq_bf16_kernel(
+                               amdgpu_waves_per_eu(DqWaves<D, DROP>::value, DqWaves<D, DROP>::value))) void dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, DropoutArgs drop) {
@@ -393,38 +399,46 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         t_lane[1][db] = &Ks[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
     }
 
-    auto step = [&](auto st, int i) {
+    // S^T and dP^T of the sub-tile in stage ST: two independent accumulator chains.
+    auto chains = [&](auto st, f32x16& s, f32x16& dp) {
         constexpr int ST = decltype(st)::value;
-        wait_vmcnt<(NS - 2) * LPS>();
-        __syncthreads();
-        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, i + NS - 1);
-        if (i >= wave_nt) return;
-        const int kv0 = i * BK;
-        f32x16 s = f32x16{}, dp = f32x16{};
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < DC; ++kc) {
             s = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE), qf[kc], s);
             dp = mfma_bf16(load_bf16x8(r_lane[kc] + ST * STAGE + V_OFF), of[kc], dp);
         }
+    };
+    // Causal (key > query) or tail (key >= N) mask of sub-tile t, as -inf scores (P = 0).
+    auto needs_mask = [&](int t) { return CAUSAL ? (t * BK + BK - 1 > wq0) : (t * BK + BK > N); };
+    auto mask = [&](int t, f32x16& s) {
+        const int kv0 = t * BK;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 8 * (r / 4) + 4 * half + (r % 4);
+            if (CAUSAL ? (key > myq) : (key >= N)) s[r] = -INFINITY;
+        }
+    };
+    // P = 2^(scale log2(e) s - lse2) and dS = P (dP - D) of sub-tile t, as bf16 B operands.
+    auto grad_scores = [&](int t, f32x16& s, f32x16& dp, bf16x8 (&sb)[2]) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-        if (CAUSAL ? (kv0 + BK - 1 > wq0) : (kv0 + BK > N)) {  // diagonal or tail sub-tile
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (CAUSAL ? (key > myq) : (key >= N)) s[r] = 0.f;
-            }
-        }
         if constexpr (DROP) {
             uint32_t dm[4];
-            dropout_bytes<true>(drop, (uint32_t)bh, myq, kv0, lane, dm);
+            dropout_bytes<true>(drop, (uint32_t)bh, myq, t * BK, lane, dm);
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] * dropout_factor(dm, r, drop) - del);
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
         }
-        const bf16x8 sb[2] = {to_bf16x8(dp, 0), to_bf16x8(dp, 8)};
+        sb[0] = to_bf16x8(dp, 0);
+        sb[1] = to_bf16x8(dp, 8);
+    };
+    // dQ^T += K^T dS^T for the sub-tile in stage ST.
+    auto dq_product = [&](auto st, const bf16x8 (&sb)[2]) {
+        constexpr int ST = decltype(st)::value;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -435,24 +449,52 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
             }
     };
 
+    // Software pipeline, as in the forward: step i (stage CUR = i % NS) holds S(i), dP(i)
+    // (masked) in `sc`, `dc`; the exponentials and dS of sub-tile i run on the VALU while the
+    // MFMAs compute S(i+1), dP(i+1) into `sn`, `dn`; then dQ += K(i)^T dS(i).  On a wave's last
+    // sub-tile the chains of sub-tile i + 1 still run (on loaded data or zeros, fully masked)
+    // and are never used.
+    auto step = [&](auto cur_st, int i, f32x16& sc, f32x16& dc, f32x16& sn, f32x16& dn) {
+        constexpr int CUR = decltype(cur_st)::value;
+        wait_vmcnt<(NS - 3) * LPS>();  // sub-tile i + 1 has landed (this wave's share)
+        __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
+        issue(std::integral_constant<int, (CUR + NS - 1) % NS>{}, i + NS - 1);
+        if (i >= wave_nt) return;
+        bf16x8 sb[2];
+        grad_scores(i, sc, dc, sb);
+        chains(std::integral_constant<int, (CUR + 1) % NS>{}, sn, dn);
+        interleave_mfma<2 * DC, 0, 4>();
+        asm volatile("" : "+v"(sb[0]), "+v"(sb[1]));  // keep the VALU work in region 1
+        dq_product(cur_st, sb);
+        if (needs_mask(i + 1)) mask(i + 1, sn);
+    };
+
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
     static_assert(NS == 4, "the loop below is unrolled over four stages");
+    static_assert((NS - 2) * LPS < 64, "pipeline depth");
     issue(S0{}, 0);
     issue(S1{}, 1);
     issue(S2{}, 2);
+    wait_vmcnt<(NS - 2) * LPS>();
+    __syncthreads();
+    f32x16 sa, da, sbb, dbb;
+    if (wave_nt > 0) {
+        chains(S0{}, sa, da);
+        if (needs_mask(0)) mask(0, sa);
+    }
     int i = 0;
     for (; i + 3 < nt; i += 4) {
-        step(S0{}, i);
-        step(S1{}, i + 1);
-        step(S2{}, i + 2);
-        step(S3{}, i + 3);
+        step(S0{}, i, sa, da, sbb, dbb);
+        step(S1{}, i + 1, sbb, dbb, sa, da);
+        step(S2{}, i + 2, sa, da, sbb, dbb);
+        step(S3{}, i + 3, sbb, dbb, sa, da);
     }
-    if (i < nt) step(S0{}, i);
-    if (i + 1 < nt) step(S1{}, i + 1);
-    if (i + 2 < nt) step(S2{}, i + 2);
+    if (i < nt) step(S0{}, i, sa, da, sbb, dbb);
+    if (i + 1 < nt) step(S1{}, i + 1, sbb, dbb, sa, da);
+    if (i + 2 < nt) step(S2{}, i + 2, sa, da, sbb, dbb);
     wait_vmcnt<0>();
 
     if (myq < N) {

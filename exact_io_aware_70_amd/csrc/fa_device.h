@@ -164,16 +164,22 @@ __device__ __forceinline__ void pin_regs(bf16x8 (&v)[A][B]) {
 }
 
 // LDS swizzle: row r of a stage stores its logical 16-byte chunk c at slot c ^ swz_row(r).
-// gfx950's LDS serves 256 bytes per clock to 128-bit reads (64 banks) and 128 bytes per
-// clock to the transposed 64-bit reads.  The K reads of the S^T product fetch one chunk
-// from 16 consecutive rows per 16 lanes, so the 16 rows must land in 16 different 16-byte
-// bank groups; the transposed V reads fetch two chunks from each of 4 consecutive rows per
-// 16 lanes, and run at full rate when those 8 pieces fill one aligned 128-byte span.
-//   D = 128 (256-byte rows): f(r) = (2r mod 8) | (r/4 mod 2) | (r mod 16 >= 8 ? 8 : 0)
+// gfx950's LDS has 64 four-byte banks (256 bytes per clock).  A 256-byte row (D = 128)
+// covers every bank once, so a row's slot is its 16-byte bank group.
+//   * Row reads (128-bit, the K / Q operands): 16 lanes fetch one logical chunk from 16
+//     consecutive rows, so swz_row must be a permutation on each aligned block of 16 rows.
+//   * Transposed reads (ds_read_b64_tr_b16, the V^T / Q^T / dO^T / K^T operands): half a
+//     wave fetches four consecutive chunks (an aligned group 4g..4g+3) from each of four
+//     consecutive rows.  XOR keeps each row's four chunks inside one aligned group, number
+//     g ^ (swz_row(r) / 4), so the four rows need four different values of swz_row(r) / 4.
+//   D = 128: swz_row(r) = 4 (r mod 4) + (r / 4 mod 4) meets both: it is a permutation of
+//            0..15, and r mod 4 picks the group.  (The earlier (2r mod 8) | (r/4 mod 2) |
+//            (r mod 16 >= 8 ? 8 : 0) met only the first and cost every transposed read a
+//            two-way conflict, SQ_LDS_BANK_CONFLICT = 2 cycles per read.)
 //   D = 64 (128-byte rows, two per 256 bytes): the same idea on row pairs.
 template <int D>
 __device__ __forceinline__ int swz_row(int r) {
-    if constexpr (D == 128) return ((2 * r) & 7) | ((r >> 2) & 1) | (r & 8);
+    if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
     const int x = (r >> 1) & 7;
     return 2 * (x & 3) + ((x >> 2) & 1);
 }
