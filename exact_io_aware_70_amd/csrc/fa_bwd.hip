@@ -187,19 +187,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             sacc = mfma_bf16(load_bf16x8(r_lane[kc] + so), kf[kc], sacc);
             pacc = mfma_bf16(load_bf16x8(r_lane[kc] + so + DO_OFF), vf[kc], pacc);
         }
+        // P first: the dV products need only P, so the scheduler can run them on the MFMA
+        // while the VALU forms dS = P (dP - D); the dK products follow.  (Pinning P before the
+        // dV products, or a scheduling hint here, pushes the kernel past 256 VGPRs.)
+        f32x4 d4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&LDs[ls][0][8 * g + 4 * half]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&LDs[ls][1][8 * g + 4 * half]);
+            d4[g] = *reinterpret_cast<const f32x4*>(&LDs[ls][1][8 * g + 4 * half]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -l4[e]));
                 if (MASKED && l32 > 8 * g + 4 * half + e) p = 0.f;
                 sacc[4 * g + e] = p;
-                if constexpr (DROP)
-                    pacc[4 * g + e] = p * (pacc[4 * g + e] * dropout_factor(dm, 4 * g + e, drop) - d4[e]);
-                else
-                    pacc[4 * g + e] = p * (pacc[4 * g + e] - d4[e]);
             }
         }
         bf16x8 pb[2] = {to_bf16x8(sacc, 0), to_bf16x8(sacc, 8)};
@@ -212,7 +212,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
                 pb[cc] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
             }
         }
-        const bf16x8 sb[2] = {to_bf16x8(pacc, 0), to_bf16x8(pacc, 8)};
         // dV^T += dO^T P, dK^T += Q^T dS: for k-step cc the B operands hold queries
         // 16cc + 8(i/4) + 4 half + i%4; the transposed reads fetch rows 16cc + tr_row (+8).
 #pragma unroll
@@ -223,6 +222,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
                 const bf16x8 a_do = join_tr(lds_read_tr16(t_lane[0][db] + off + DO_OFF),
                                             lds_read_tr16(t_lane[1][db] + off + DO_OFF));
                 dv[db] = mfma_bf16(a_do, pb[cc], dv[db]);
+            }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = sacc[4 * g + e];
+                if constexpr (DROP)
+                    pacc[4 * g + e] = p * (pacc[4 * g + e] * dropout_factor(dm, 4 * g + e, drop) - d4[g][e]);
+                else
+                    pacc[4 * g + e] = p * (pacc[4 * g + e] - d4[g][e]);
+            }
+        const bf16x8 sb[2] = {to_bf16x8(pacc, 0), to_bf16x8(pacc, 8)};
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int off = so + 16 * cc * D;
                 const bf16x8 a_q = join_tr(lds_read_tr16(t_lane[0][db] + off), lds_read_tr16(t_lane[1][db] + off));
                 dk[db] = mfma_bf16(a_q, sb[cc], dk[db]);
             }
