@@ -22,6 +22,11 @@ Gaussian q and k scaled by 1/sqrt(d) are N(0, 1)):
   softmax_bf16_r65536_c8192     bf16   65536   8192  11   (8 heads' score rows at N = 8192)
   softmax_f32_r8192_c2048       f32    8192    2048  12
 
+Tensors past 2^31 elements (the 64-bit offset case: B=1, H=4104, N=4096, d=128,
+4.3 GB per bf16 tensor) are drawn on the GPU by ``device_normal_bf16``: torch's
+seeded device generator, N(0, 1) in fp32, rounded to bf16.  Tests copy the heads they
+check back to the host, so the oracle still sees the stored values.
+
 Recipe: ``np.random.default_rng(seed).standard_normal(shape, dtype=float32)`` drawn
 in the order Q, K, V (then dO for backward cases); Q multiplied by ``q_scale`` in
 fp32; then rounded to the storage dtype (bf16 with round-to-nearest-even).  The
@@ -174,3 +179,11 @@ def make_fp8_case(B: int, H: int, N: int, d: int, seed: int, q_scale: float = 1.
         codes = e4m3_codes(x * sc[:, :, None, None])
         case[name] = {"codes": codes, "descale": (np.float32(1.0) / sc).astype(np.float32)}
     return case
+
+
+def device_normal_bf16(shape, generator, device="cuda"):
+    """A bf16 tensor of N(0, 1) draws made on the GPU by ``generator`` (a seeded
+    ``torch.Generator`` on ``device``): fp32 draws rounded to bf16 (RNE).  For inputs too
+    large to draw on the host; successive calls continue the generator's stream."""
+    import torch
+    return torch.randn(tuple(shape), generator=generator, device=device, dtype=torch.float32).to(torch.bfloat16)
