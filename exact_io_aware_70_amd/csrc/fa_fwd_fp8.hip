@@ -150,8 +150,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         v_lane[db] = &Vs[0][tr_r * D + (((2 * db + ((lane >> 4) & 1)) ^ swz8_row(tr_r)) << 4) + 8 * (lane & 1)];
-    const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0 in every byte
+    // E4M3 1.0 in every byte.  Not const: an empty asm after each use keeps it in its eight
+    // registers (otherwise the compiler rebuilds them from one register at every tile).
+    i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                  0x38383838, 0x38383838, 0x38383838, 0x38383838};
 
     // S^T of the tile in stage ST: s[kb] covers keys 32 kb .. 32 kb + 31 (lane = query, register
     // r = key 32 kb + 8(r/4) + 4 half + r%4); the two key blocks are independent chains.
@@ -197,7 +199,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
             for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, -m_ref));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][4 * j], s[kb][4 * j + 1], 0, false);
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][4 * j], s[kb][4 * j + 1], pb[4 * kb + j], false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][4 * j + 2], s[kb][4 * j + 3], w, true);
                 pb[4 * kb + j] = w;
             }
@@ -215,6 +217,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
             oacc[db] = mfma_fp8(a, pb, oacc[db]);
         }
         lacc = mfma_fp8(ones, pb, lacc);
+        asm volatile("" : "+v"(ones));
     };
 
     using S0 = std::integral_constant<int, 0>;
@@ -236,6 +239,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
         raise_ref(sa);
     }
 
+    // P of the current tile, carried across steps: each word's first conversion names the
+    // register it overwrites as the preserved half (both halves are rewritten), so no
+    // zeroing instruction precedes it.
+    i32x8 pb = {};
     // One pipeline step on tile i (stage CUR = i % NS): `cur` holds S(i) (masked, reference
     // raised); leaves S(i+1) in `nxt`.  Every wave runs every step (barriers and loads are
     // collective); the arithmetic stops after the wave's own last tile.  On that last tile
@@ -247,7 +254,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
         __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
         issue(std::integral_constant<int, (CUR + NS - 1) % NS>{}, i + NS - 1);
         if (i >= wave_nt) return;
-        i32x8 pb;
         probs(cur, pb);
         scores(std::integral_constant<int, (CUR + 1) % NS>{}, nxt);
         interleave_mfma<4, 0, 16>();
