@@ -134,6 +134,38 @@ def load_traffic(workload):
     return data["kernels"]
 
 
+def util_file(workload):
+    return os.path.join(ROOT, "profiles", f"mfma_util_{workload}.json")
+
+
+def load_util(workload):
+    """MFMA busy share and clock per kernel from the committed SQ counter summary, if still current."""
+    path = util_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_sha256") != sources_digest(workload):
+        return None
+    return data["kernels"]
+
+
+def add_measured(entry, name, traffic, util):
+    """Add to one kernel entry what the counters measured for it: HBM GB/s (counter bytes over
+    the live launch time, against the 8 TB/s peak) and the matrix cores' busy share at the
+    clock the kernel ran; null where no current counter summary exists."""
+    tb = traffic.get(name, {}).get("bytes") if traffic else None
+    entry["traffic"] = tb
+    gbs = tb / (entry["ms"] * 1e-3) / 1e9 if tb else None
+    entry["hbm_gbs"] = round(gbs, 1) if gbs else None
+    entry["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4) if gbs else None
+    u = util.get(name) if util else None
+    if entry.get("bound") == "mfma":
+        entry["mfma_busy"] = u["mfma_busy"] if u else None
+        entry["clock_ghz"] = u["clock_ghz"] if u else None
+    return entry
+
+
 def summarize_pmc(args):
     """Average FETCH_SIZE / WRITE_SIZE per dispatch of each kernel, scaled by the copy kernel."""
     def read(dirname, counter):
@@ -270,6 +302,7 @@ def summarize_sq(args):
               "| kernel | ms | clock (GHz) | MFMA instr. / algorithmic | MFMA busy | MFMA busy with VALU co-issue "
               "| other VALU instr. per MFMA (exp included) | exp per MFMA | LDS instr. per MFMA | CU busy |",
               "|---|---|---|---|---|---|---|---|---|---|"]
+    summary = {}
     for n in ("fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"):
         k = c.get(n, {})
         if "GRBM_GUI_ACTIVE" not in k or n not in dur:
@@ -288,6 +321,7 @@ def summarize_sq(args):
         cu = k.get("SQ_BUSY_CU_CYCLES", float("nan")) / (256.0 * cyc)
         lines.append(f"| {n} | {dur[n] * 1e3:.3f} | {clock:.2f} | {mfma / algo:.3f} | {busy:.1%} | {coex:.1%} "
                      f"| {valu:.2f} | {trans:.2f} | {lds:.2f} | {cu:.1%} |")
+        summary[n] = {"mfma_busy": round(busy, 4), "clock_ghz": round(clock, 3), "valu_coissue": round(coex, 4)}
     lines += ["", "Raw means per dispatch:", "", "| kernel | counter | value |", "|---|---|---|"]
     for n in sorted(c):
         for counter in sorted(c[n]):
@@ -295,6 +329,10 @@ def summarize_sq(args):
     path = os.path.join(ROOT, "profiles", f"mfma_util_{args.workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
+    with open(util_file(args.workload), "w") as f:
+        json.dump({"workload": args.workload, "source_sha256": sources_digest(args.workload),
+                   "from": os.path.basename(path), "kernels": summary}, f, indent=1)
+        f.write("\n")
     print("\n".join(lines))
 
 
@@ -439,7 +477,10 @@ def bench_fp8(args):
     ms_step = wall * 1e3 / args.steps
     ach = ff / (avg * 1e-3) / 1e12
     traffic = load_traffic(args.workload)
-    tb = traffic.get("fwd_fp8_kernel", {}).get("bytes") if traffic else None
+    kd8 = add_measured({"ms": round(avg, 4), "ms_min": round(min(ms), 4), "bound": "mfma", "achieved": round(ach, 2),
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4),
+                        "units_per_launch": ff}, "fwd_fp8_kernel", traffic, load_util(args.workload))
+    tb = kd8["traffic"]
     out = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved), E4M3 inputs",
         "value": round(ff / (ms_step * 1e-3) / 1e12, 2),
@@ -455,10 +496,7 @@ def bench_fp8(args):
         "data": "synthetic (seeded N(0,1) Q/K/V, Q x%g, quantised to E4M3 per head)" % c["q_scale"],
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal, "pass": "fwd",
                    "step_flops": ff},
-        "kernels": {"fwd_fp8_kernel": {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "bound": "mfma",
-                                       "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": round(ach / PEAK_FP8_TFLOPS, 4), "units_per_launch": ff,
-                                       "traffic": tb}},
+        "kernels": {"fwd_fp8_kernel": kd8},
         "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": tb,
                      "launch_ms": round(avg, 4)},
@@ -530,10 +568,10 @@ def bench_softmax(args):
         "dtype": c["dtype"],
         "data": "synthetic (seeded N(0,1) logits)",
         "config": {"workload": args.workload, "rows": c["rows"], "cols": c["cols"], "bytes_per_step": nbytes},
-        "kernels": {"softmax_rows_kernel": {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "bound": "hbm",
-                                            "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                            "frac": round(ach / PEAK_HBM_GBS, 4), "units_per_launch": nbytes,
-                                            "traffic": tb}},
+        "kernels": {"softmax_rows_kernel": add_measured(
+            {"ms": round(avg, 4), "ms_min": round(min(ms), 4), "bound": "hbm", "achieved": round(ach, 2),
+             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "units_per_launch": nbytes},
+            "softmax_rows_kernel", traffic, None)},
         "roofline": {"kernel": "softmax_rows_kernel", "bound": "hbm", "achieved": round(ach, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": tb,
                      "launch_ms": round(avg, 4)},
@@ -641,6 +679,7 @@ def main():
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if case["dtype"] == "bf16" else PEAK_F32_TFLOPS
     traffic = load_traffic(args.workload) if drop == 0.0 else None  # counters cover the plain kernels
+    util = load_util(args.workload) if drop == 0.0 else None
 
     kernels = {}
     for name in knames:
@@ -650,10 +689,9 @@ def main():
             ach, pk, u = rate / 1e12, peak, "TFLOP/s"
         else:
             ach, pk, u = rate / 1e9, PEAK_HBM_GBS, "GB/s"
-        tb = traffic.get(name, {}).get("bytes") if traffic else None
-        kernels[name] = {"ms": round(avg[name], 4), "ms_min": round(min(per[name]), 4), "bound": bound,
-                         "achieved": round(ach, 2), "peak": pk, "unit": u, "frac": round(ach / pk, 4),
-                         "units_per_launch": units, "traffic": tb}
+        kernels[name] = add_measured({"ms": round(avg[name], 4), "ms_min": round(min(per[name]), 4),
+                                      "bound": bound, "achieved": round(ach, 2), "peak": pk, "unit": u,
+                                      "frac": round(ach / pk, 4), "units_per_launch": units}, name, traffic, util)
     dom = max(knames, key=lambda n: avg[n])
     kd = kernels[dom]
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],

@@ -88,3 +88,21 @@ def test_softmax_units_and_digest():
     assert bench.softmax_bytes(3, 5, "f32") == 2 * 3 * 5 * 4 + 12
     assert bench.is_softmax("softmax_bf16_r65536_c8192") and not bench.is_softmax("fwd_bf16_causal_b4h32_n8192_d128")
     assert bench.sources_digest("softmax_bf16_r65536_c8192") != bench.sources_digest("fwd_bf16_causal_b4h32_n8192_d128")
+
+
+def test_measured_rates_come_from_current_summaries_only(tmp_path, monkeypatch):
+    """A kernel entry gains HBM GB/s (counter bytes over the live launch time) and the MFMA
+    busy share and clock of the committed SQ summary; with a stale digest both are null."""
+    util = tmp_path / "util.json"
+    monkeypatch.setattr(bench, "util_file", lambda w: str(util))
+    util.write_text(json.dumps({"source_sha256": bench.sources_digest("synthetic"),
+                                "kernels": {"dq_bf16_kernel": {"mfma_busy": 0.5, "clock_ghz": 1.7}}}))
+    traffic = {"dq_bf16_kernel": {"bytes": 2_000_000_000}}
+    e = bench.add_measured({"ms": 2.0, "bound": "mfma"}, "dq_bf16_kernel", traffic, bench.load_util("synthetic"))
+    assert e["traffic"] == 2_000_000_000 and e["hbm_gbs"] == 1000.0 and e["hbm_frac"] == 0.125
+    assert e["mfma_busy"] == 0.5 and e["clock_ghz"] == 1.7
+    util.write_text(json.dumps({"source_sha256": "0" * 64, "kernels": {}}))
+    e = bench.add_measured({"ms": 2.0, "bound": "mfma"}, "dq_bf16_kernel", None, bench.load_util("synthetic"))
+    assert e["traffic"] is None and e["hbm_gbs"] is None and e["mfma_busy"] is None
+    h = bench.add_measured({"ms": 1.0, "bound": "hbm"}, "delta_kernel", {"delta_kernel": {"bytes": 8e9}}, None)
+    assert h["hbm_gbs"] == 8000.0 and "mfma_busy" not in h
