@@ -43,10 +43,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
+# What a workload's counter summaries are keyed to: its kernel sources and the build script
+# (compiler flags change the code as much as the sources do).
+BUILD_SCRIPT = "exact_io_aware_70_amd/build.py"
 KERNEL_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd.hip", "exact_io_aware_70_amd/csrc/fa_bwd.hip",
-                  "exact_io_aware_70_amd/csrc/fa_device.h", "exact_io_aware_70_amd/csrc/fa_dropout.h"]
-SOFTMAX_SOURCES = ["exact_io_aware_70_amd/csrc/fa_softmax.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
-FP8_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_70_amd/csrc/fa_device.h"]
+                  "exact_io_aware_70_amd/csrc/fa_device.h", "exact_io_aware_70_amd/csrc/fa_dropout.h", BUILD_SCRIPT]
+SOFTMAX_SOURCES = ["exact_io_aware_70_amd/csrc/fa_softmax.hip", "exact_io_aware_70_amd/csrc/fa_device.h",
+                   BUILD_SCRIPT]
+FP8_SOURCES = ["exact_io_aware_70_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_70_amd/csrc/fa_device.h", BUILD_SCRIPT]
 
 
 DEFAULT_WORKLOAD = "fwd_bf16_causal_b4h32_n8192_d128"
