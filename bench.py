@@ -117,9 +117,16 @@ def kernel_table(dtype, B, H, N, d, causal):
         "delta_kernel": ("hbm", 2.0 * B * H * N * d * elt + 12.0 * B * H * N, "byte"),
         # four products: S, dP, dV += P^T dO, dK += dS^T Q
         f"dkdv_{sfx}_kernel": ("mfma", 8.0 * n2d, "flop"),
-        # three products: S and dP (recomputed) and dQ += dS K
-        f"dq_{sfx}_kernel": ("mfma", 6.0 * n2d, "flop"),
+        # one product of the method: dQ += dS K.  The kernel also recomputes S and dP, the
+        # price of a backward without atomics; those flops are not algorithmic units and are
+        # reported apart (EXECUTED_FACTOR)
+        f"dq_{sfx}_kernel": ("mfma", 2.0 * n2d, "flop"),
     }
+
+
+# Executed over algorithmic flops, for kernels that recompute products: the dQ kernel runs
+# three products (S, dP, dQ) for the one it contributes.
+EXECUTED_FACTOR = {"dq_bf16_kernel": 3.0, "dq_f32_kernel": 3.0}
 
 
 def traffic_file(workload):
@@ -696,6 +703,10 @@ def main():
         kernels[name] = add_measured({"ms": round(avg[name], 4), "ms_min": round(min(per[name]), 4),
                                       "bound": bound, "achieved": round(ach, 2), "peak": pk, "unit": u,
                                       "frac": round(ach / pk, 4), "units_per_launch": units}, name, traffic, util)
+        if name in EXECUTED_FACTOR:
+            ex = EXECUTED_FACTOR[name] * units
+            kernels[name]["executed_flops"] = ex
+            kernels[name]["executed_tflops"] = round(ex / (avg[name] * 1e-3) / 1e12, 2)
     dom = max(knames, key=lambda n: avg[n])
     kd = kernels[dom]
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"], "peak": kd["peak"],

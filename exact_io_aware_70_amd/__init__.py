@@ -109,6 +109,38 @@ def _check(name: str, t, shape, dtype, device):
         raise ValueError(f"{name}: must be contiguous")
 
 
+def _workspace(workspace, need: int, device):
+    """The caller's backward workspace, checked (on `device`, contiguous, >= need bytes), or a
+    new one.  The C side sees only a raw pointer and a byte count."""
+    import torch
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.device != device:
+        raise ValueError(f"workspace: on {workspace.device}, expected {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    have = workspace.numel() * workspace.element_size()
+    if have < need:
+        raise ValueError(f"workspace: {have} bytes, fa_bwd_workspace_size gives {need}")
+    return workspace
+
+
+def _event_handles(events, stream, device):
+    """ctypes array of the FA_BWD_LAUNCHES + 1 torch events' HIP handles (None passes through)."""
+    import torch
+    if events is None:
+        return None
+    if len(events) != FA_BWD_LAUNCHES + 1:
+        raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    handles = (ctypes.c_void_p * len(events))()
+    for n, ev in enumerate(events):
+        if ev.cuda_event == 0:  # torch creates the underlying event on its first record
+            ev.record(s)
+        handles[n] = ev.cuda_event
+    return handles
+
+
 def _stream_handle(stream, device):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream(device)
@@ -166,9 +198,9 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=Fa
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check(name, t, (B, H, N, d), q.dtype, dev)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_size(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, fa_bwd_workspace_size(B, H, N, d, code), dev)
+    if events is not None and len(events) != FA_BWD_LAUNCHES + 1:
+        raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0, code,
@@ -177,15 +209,7 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=Fa
         st = lib.fa_bwd(*args)
         where = "fa_bwd"
     else:
-        if len(events) != FA_BWD_LAUNCHES + 1:
-            raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
-        handles = (ctypes.c_void_p * len(events))()
-        for n, ev in enumerate(events):
-            if ev.cuda_event == 0:  # torch creates the underlying event on its first record
-                ev.record(s)
-            handles[n] = ev.cuda_event
-        st = lib.fa_bwd_timed(*args, handles)
+        st = lib.fa_bwd_timed(*args, _event_handles(events, stream, dev))
         where = "fa_bwd_timed"
     if st != FA_OK:
         raise FAError(st, where)
@@ -284,20 +308,14 @@ def fa_bwd_dropout(q, k, v, o, lse, do, dropout_p, seed, offset=0, dq=None, dk=N
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
     code = _dtype_code(q)
-    if workspace is None:
-        workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d, code), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, fa_bwd_workspace_size(B, H, N, d, code), dev)
+    if events is not None and len(events) != FA_BWD_LAUNCHES + 1:
+        raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    handles = None
-    if events is not None:
-        if len(events) != FA_BWD_LAUNCHES + 1:
-            raise ValueError(f"events: need {FA_BWD_LAUNCHES + 1} events")
-        s = stream if stream is not None else torch.cuda.current_stream(dev)
-        handles = (ctypes.c_void_p * len(events))()
-        for n, ev in enumerate(events):
-            if ev.cuda_event == 0:
-                ev.record(s)
-            handles[n] = ev.cuda_event
+    handles = _event_handles(events, stream, dev)
     st = lib.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0, code,
                             float(dropout_p), int(seed), int(offset), workspace.data_ptr(),

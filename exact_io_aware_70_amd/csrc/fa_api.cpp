@@ -13,15 +13,21 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+constexpr int kMaxN = FA_MAX_N;
+constexpr long long kMaxTiles = FA_MAX_TILES;  // B * H * ceil(N / 64)
+
 // Checks shared by the forward and backward entry points.
 int check_common(int B, int H, int N, int d, float scale, int dtype) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (!(scale > 0.0f) || !std::isfinite(scale)) return FA_ERR_UNSUPPORTED;
-    // One workgroup per (batch, head, 64-row tile) at most: keep the 1-D grid in range.
-    const long long tiles = (long long)B * H * ((N + 63) / 64);
-    if (tiles > 0x7fffffffLL) return FA_ERR_SHAPE;
+    // Row and key indices stay far from int overflow (the kernels form N + 128 and the like).
+    if (N > kMaxN) return FA_ERR_SHAPE;
+    // The attention kernels launch one 256-thread workgroup per (batch, head, tile of at least
+    // 64 rows); a dispatch holds fewer than 2^32 work-items, so fewer than 2^24 workgroups.
+    const long long tiles = (long long)B * H * (((long long)N + 63) / 64);
+    if (tiles > kMaxTiles) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
@@ -85,7 +91,10 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
                       workspace_bytes, stream, events);
 }
 
-// Dropout parameters: p in [0, 1); threshold round(256 p); key from the 64-bit seed.
+// Dropout parameters: p in [0, 1); threshold t = round(256 p); key from the 64-bit seed.
+// An element is kept with probability (256 - t) / 256 exactly, so kept values are scaled by
+// 256 / (256 - t), which makes the expected keep factor exactly 1 (0 when t = 256: nothing
+// is kept).
 static bool make_dropout(float p, unsigned long long seed, unsigned offset, fa::DropoutArgs* d) {
     if (!(p >= 0.0f && p < 1.0f)) return false;
     const double t = std::floor(256.0 * (double)p + 0.5);
@@ -93,7 +102,7 @@ static bool make_dropout(float p, unsigned long long seed, unsigned offset, fa::
     d->k1 = (uint32_t)(seed >> 32);
     d->offset = offset;
     d->thr = (uint32_t)(t < 0.0 ? 0.0 : (t > 256.0 ? 256.0 : t));
-    d->inv_keep = 1.0f / (1.0f - p);
+    d->inv_keep = d->thr < 256 ? 256.0f / (float)(256 - d->thr) : 0.0f;
     return true;
 }
 
@@ -167,7 +176,7 @@ const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be >= 1 and the grid must fit in 2^31 - 1 workgroups";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be >= 1, N <= 2^30 and B*H*ceil(N/64) < 2^24";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64 or 128, dtype FA_F32 or FA_BF16, scale finite and > 0 (dropout: bf16, 0 <= p < 1; FP8: d = 128)";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned (lse 4-byte)";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than fa_bwd_workspace_size()";

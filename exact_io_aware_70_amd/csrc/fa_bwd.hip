@@ -29,15 +29,17 @@ namespace {
 // ------------------------------------------------------------------ delta = rowsum(dO * O)
 // Also writes lse2 = lse * log2(e), the form in which the recomputing kernels use lse
 // (P = 2^(scale log2(e) s - lse2)), so they need no per-score conversion.
+// Rows row0 + blockIdx.x * RPB + ... of the flat [B * H * N] row range (the host splits very
+// long ranges over several launches: a dispatch holds fewer than 2^32 work-items).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                      const float* __restrict__ LSE, float* __restrict__ Delta,
-                                                     float* __restrict__ LSE2, long long rows) {
+                                                     float* __restrict__ LSE2, long long row0, long long rows) {
     constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
     constexpr int CPR = D / EPC;         // chunks (threads) per row
     constexpr int RPB = 256 / CPR;       // rows per block
     const int tid = threadIdx.x;
-    const long long row = (long long)blockIdx.x * RPB + tid / CPR;
+    const long long row = row0 + (long long)blockIdx.x * RPB + tid / CPR;
     const int c = tid % CPR;
     float acc = 0.f;
     if (row < rows) {
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
 // Query rows past N load as zeros with lse = D = 0: their P is 1 but multiplies zero dO
 // rows, and their dS = P (0 - 0) = 0, so they contribute nothing.
 // DROP: dropout (dV takes the dropped P; dS = P (Z dP - D) with Z the keep factor; the
-// 1 / (1 - p) of dV is applied at the store).
+// keep scale of dV is applied at the store).
 template <int D, int NW, bool CAUSAL, bool DROP>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -145,7 +147,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     auto issue = [&](auto st, int t) {
         constexpr int ST = decltype(st)::value;
         const int q0 = t < 0 ? N : t * BQ;  // past the end: zero rows, the loads read zeros
-        const uint32_t rows = (uint32_t)max(0, N - q0);
+        // Each resource spans only this sub-tile (at most BQ rows): the 32-bit byte count
+        // cannot wrap however long the sequence is.
+        const uint32_t rows = (uint32_t)min(max(0, N - q0), BQ);
         const i32x4 rq = make_rsrc(Q + base + (size_t)min(q0, N) * D, rows * D * 2);
         const i32x4 ro = make_rsrc(dO + base + (size_t)min(q0, N) * D, rows * D * 2);
 #pragma unroll
@@ -153,8 +157,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             load_lds_b128(rq, lds_addr(&Qs[ST][(j * NT + wave * 64) * 8]), voff[j]);
             load_lds_b128(ro, lds_addr(&dOs[ST][(j * NT + wave * 64) * 8]), voff[j]);
         }
-        const i32x4 rl = make_rsrc(LSE2 + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
-        const i32x4 rd = make_rsrc(Delta + rbase + min(q0, N), min(rows, (uint32_t)BQ) * 4);
+        const i32x4 rl = make_rsrc(LSE2 + rbase + min(q0, N), rows * 4);
+        const i32x4 rd = make_rsrc(Delta + rbase + min(q0, N), rows * 4);
         load_lds_b32(rl, lds_addr(&LDs[ST][0][0]), (uint32_t)(lane * 4));
         load_lds_b32(rd, lds_addr(&LDs[ST][1][0]), (uint32_t)(lane * 4));
     };
@@ -283,7 +287,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             // The diagonal sub-tile (query rows kw0 .. kw0 + 31) into this wave's own stage;
             // only this wave reads it, so its own vmcnt wait is enough.
             const int q0 = kw0;
-            const uint32_t rows = (uint32_t)max(0, N - q0);
+            const uint32_t rows = (uint32_t)min(max(0, N - q0), BQ);  // one sub-tile: never wraps
             const i32x4 rq = make_rsrc(Q + base + (size_t)q0 * D, rows * D * 2);
             const i32x4 ro = make_rsrc(dO + base + (size_t)q0 * D, rows * D * 2);
 #pragma unroll
@@ -293,8 +297,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
                 load_lds_b128(rq, lds_addr(&Qs[wave][j * 64 * 8]), vo);
                 load_lds_b128(ro, lds_addr(&dOs[wave][j * 64 * 8]), vo);
             }
-            const i32x4 rl = make_rsrc(LSE2 + rbase + q0, min(rows, (uint32_t)BQ) * 4);
-            const i32x4 rd = make_rsrc(Delta + rbase + q0, min(rows, (uint32_t)BQ) * 4);
+            const i32x4 rl = make_rsrc(LSE2 + rbase + q0, rows * 4);
+            const i32x4 rd = make_rsrc(Delta + rbase + q0, rows * 4);
             load_lds_b32(rl, lds_addr(&LDs[wave][0][0]), (uint32_t)(lane * 4));
             load_lds_b32(rd, lds_addr(&LDs[wave][1][0]), (uint32_t)(lane * 4));
             wait_vmcnt<0>();
@@ -392,7 +396,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     auto issue = [&](auto st, int t) {
         constexpr int ST = decltype(st)::value;
         const int kv0 = t * BK;
-        const uint32_t bytes = (uint32_t)max(0, N - kv0) * D * 2;
+        const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D * 2;  // one sub-tile: never wraps
         const i32x4 rk = make_rsrc(K + base + (size_t)min(kv0, N) * D, bytes);
         const i32x4 rv = make_rsrc(V + base + (size_t)min(kv0, N) * D, bytes);
 #pragma unroll
@@ -694,11 +698,16 @@ template <typename T, int D>
 hipError_t launch_delta(const BwdArgs& a, hipStream_t st) {
     constexpr int CPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / CPR;
+    constexpr long long kMaxGrid = 1LL << 22;  // workgroups per launch (2^30 work-items)
     const long long rows = (long long)a.B * a.H * a.N;
-    const long long grid = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)a.o, (const T*)a.dout,
-                       a.lse, a.delta, a.lse2, rows);
-    return hipGetLastError();
+    for (long long r0 = 0; r0 < rows; r0 += kMaxGrid * RPB) {
+        const long long grid = min((rows - r0 + RPB - 1) / RPB, kMaxGrid);
+        hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, (const T*)a.o,
+                           (const T*)a.dout, a.lse, a.delta, a.lse2, r0, rows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Record the caller's timing event `i` (if any) on the stream.

@@ -1,13 +1,14 @@
 // Dropout masks for the attention kernels (gfx950): Philox4x32-10 and the lane exchanges
 // that give each lane the mask bytes of the scores it holds.
 //
-// "How FlashAttention Actually Works" -- "Why Attention Is Slow" lists dropout among the
-// steps a fused attention kernel runs on chip.  The random numbers are Philox4x32-10
+// "How FlashAttention Actually Works" -- "The GPU Memory Wall: HBM vs. SRAM" lists dropout
+// among the steps of attention that a fused kernel keeps on chip.  The random numbers are Philox4x32-10
 // (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).
 // Mask of head bh: one call with counter (j >> 2, i >> 2, bh, offset) and key (seed lo,
 // seed hi) covers the 4 x 4 block of (query i, key j); element (i, j) is byte (j & 3) of
 // output word (i & 3), kept iff it is >= t = round(256 p).  Kept probabilities are scaled
-// by 1 / (1 - p) (the kernels fold that into their outputs).
+// by 256 / (256 - t), the reciprocal of the exact keep probability (the kernels fold that
+// into their outputs).
 //
 // Score layouts (32 x 32 MFMA accumulators, half = lane / 32):
 //   query per lane (forward, dQ: S^T):  register r of lane (query, half) is key
@@ -125,7 +126,7 @@ __device__ __forceinline__ void dropout_apply_bf16(uint32_t (&p)[4], uint32_t m_
     }
 }
 
-// Dropout factor of register r (the layout above): 1 / (1 - p) if kept, else 0.
+// Dropout factor of register r (the layout above): the keep scale if kept, else 0.
 __device__ __forceinline__ float dropout_factor(const uint32_t (&m)[4], int r, const DropoutArgs& d) {
     const uint32_t b = (m[r >> 2] >> (8 * (r & 3))) & 0xFFu;
     return b >= d.thr ? d.inv_keep : 0.f;

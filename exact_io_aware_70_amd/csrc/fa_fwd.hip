@@ -52,7 +52,7 @@ struct FwdTile {
 // d = 64 the kernel needs under 128 VGPRs and a 32 KiB ring, so four waves per SIMD (three
 // with dropout, whose mask needs more registers) hide more latency.
 // DROP: dropout of the probabilities in the P V product (the row sums, hence lse, stay
-// undropped; the 1 / (1 - p) scale is folded into the epilogue).
+// undropped; the keep scale is folded into the epilogue).
 template <int D, bool DROP>
 struct FwdWaves : std::integral_constant<int, D == 64 ? (DROP ? 3 : 4) : 2> {};
 
@@ -121,7 +121,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     auto issue = [&](auto st, int t) {
         constexpr int ST = decltype(st)::value;
         const int kv0 = t * BK;
-        const uint32_t bytes = (uint32_t)max(0, N - kv0) * D * 2;
+        // Each resource spans only its own sub-tile (at most BK rows), so the 32-bit byte
+        // count cannot wrap however long the sequence is.
+        const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D * 2;
         const i32x4 rk = make_rsrc(Kh + (size_t)min(kv0, N) * D, bytes);
         const i32x4 rv = make_rsrc(Vh + (size_t)min(kv0, N) * D, bytes);
 #pragma unroll

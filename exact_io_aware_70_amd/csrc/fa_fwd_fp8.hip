@@ -118,7 +118,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
     auto issue = [&](auto st, int t) {
         constexpr int ST = decltype(st)::value;
         const int kv0 = t * BK;
-        const uint32_t bytes = (uint32_t)max(0, N - kv0) * D;
+        const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D;  // one sub-tile: never wraps
         const i32x4 rk = make_rsrc(Kh + (size_t)min(kv0, N) * D, bytes);
         const i32x4 rv = make_rsrc(Vh + (size_t)min(kv0, N) * D, bytes);
 #pragma unroll

@@ -11,7 +11,7 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
 // Dropout of the probabilities (see fa_dropout.h): Philox key, counter word 3, 8-bit keep
-// threshold (keep iff byte >= thr) and 1 / (1 - p).
+// threshold (keep iff byte >= thr) and the keep scale 256 / (256 - thr).
 struct DropoutArgs {
     uint32_t k0, k1;
     uint32_t offset;

@@ -198,13 +198,16 @@ __device__ __forceinline__ float vsum_exp(u32x4 w, float ms, float s) {
 // KV raw vectors per lane are held (STREAM = false: the whole row; STREAM = true: one chunk
 // at a time).  Each 256-thread workgroup serves 256 / TEAM rows.
 template <typename T, int TEAM, int KV, bool STREAM>
+// Row r = row0 + blockIdx.x * RPW + ...: the host splits very long row ranges over several
+// launches (a dispatch holds fewer than 2^32 work-items).
 __global__ __launch_bounds__(256) void softmax_rows_kernel(const T* __restrict__ x, T* __restrict__ y,
-                                                           float* __restrict__ lse, long long rows, int cols) {
+                                                           float* __restrict__ lse, long long row0, long long rows,
+                                                           int cols) {
     constexpr int VE = Vec16<T>::VE;
     constexpr int RPW = 256 / TEAM;
     __shared__ float red[4];
     const int t = threadIdx.x % TEAM;
-    const long long r = (long long)blockIdx.x * RPW + threadIdx.x / TEAM;
+    const long long r = row0 + (long long)blockIdx.x * RPW + threadIdx.x / TEAM;
     // A team past the last row leaves at once: with TEAM = 256 that is the whole workgroup,
     // and TEAM = 64 reductions stay inside the wave, so no barrier is left waiting.
     if (r >= rows) return;
@@ -287,10 +290,15 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(const T* __restrict__
 template <typename T, int TEAM, int KV, bool STREAM>
 hipError_t launch_shape(const SoftmaxArgs& a, hipStream_t st) {
     constexpr int RPW = 256 / TEAM;
-    const long long grid = (a.rows + RPW - 1) / RPW;
-    hipLaunchKernelGGL((softmax_rows_kernel<T, TEAM, KV, STREAM>), dim3((unsigned)grid), dim3(256), 0, st,
-                       static_cast<const T*>(a.x), static_cast<T*>(a.y), a.lse, a.rows, a.cols);
-    return hipGetLastError();
+    constexpr long long kMaxGrid = 1LL << 22;  // workgroups per launch (2^30 work-items)
+    for (long long r0 = 0; r0 < a.rows; r0 += kMaxGrid * RPW) {
+        const long long grid = min((a.rows - r0 + RPW - 1) / RPW, kMaxGrid);
+        hipLaunchKernelGGL((softmax_rows_kernel<T, TEAM, KV, STREAM>), dim3((unsigned)grid), dim3(256), 0, st,
+                           static_cast<const T*>(a.x), static_cast<T*>(a.y), a.lse, r0, a.rows, a.cols);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename T>

@@ -31,7 +31,12 @@
  *     probabilities and dS are rounded to bf16 before their products; outputs are
  *     rounded to the input dtype (round to nearest even).  The fp32 path uses fp32
  *     MFMA throughout.
- *   - Supported: B, H, N >= 1; d in {64, 128}; B*H*ceil(N/64) < 2^31.
+ *   - Supported: B, H, N >= 1; N <= FA_MAX_N (2^30); d in {64, 128};
+ *     B*H*ceil(N/64) <= FA_MAX_TILES (2^24 - 1: every attention launch is one 256-thread
+ *     workgroup per tile of at least 64 rows, and a dispatch holds fewer than 2^32
+ *     work-items).  Sizes outside this return FA_ERR_SHAPE.  Inside it no index or byte
+ *     count wraps: tensor offsets are 64-bit, and each range-checked tile load spans only
+ *     its own tile.
  *   (fa_softmax_rows, below, has conventions of its own.)
  *   - Errors: arguments are validated before anything is enqueued; on failure a
  *     negative fa_status is returned and nothing runs.  A failed kernel launch returns
@@ -50,10 +55,13 @@ extern "C" {
 
 #define FA_VERSION 100 /* 1.0.0 */
 
+#define FA_MAX_N (1 << 30)               /* largest sequence length accepted */
+#define FA_MAX_TILES ((1LL << 24) - 1)   /* largest B * H * ceil(N / 64) accepted */
+
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = -1,        /* a required pointer is NULL */
-    FA_ERR_SHAPE = -2,       /* a size < 1, or the grid would exceed 2^31 - 1 workgroups */
+    FA_ERR_SHAPE = -2,       /* a size < 1, N > FA_MAX_N, or B*H*ceil(N/64) > FA_MAX_TILES */
     FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128} or unknown dtype */
     FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
     FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than fa_bwd_workspace_size() */
@@ -74,7 +82,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (>= 256; 0 if the sizes are
- * invalid).  Only the size matters; the contents need no initialisation.
+ * invalid).  Only the size matters; the contents need no initialisation.  Plumbing: no
+ * page defines it.  The workspace holds D_i = rowsum(dout * o) and lse * log2(e), one float
+ * each per (batch, head, row), each array rounded up to 256 bytes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
 
@@ -113,15 +123,17 @@ int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, con
 
 /*
  * Forward and backward passes with dropout on the probabilities ("How FlashAttention
- * Actually Works" -- "Why Attention Is Slow": dropout is one of the steps a fused kernel
- * runs on chip).  The same arguments and behaviour as fa_fwd / fa_bwd (fa_bwd_timed when
+ * Actually Works" -- "The GPU Memory Wall: HBM vs. SRAM": dropout is one of the steps of
+ * attention that a fused kernel keeps on chip).  The same arguments and behaviour as fa_fwd / fa_bwd (fa_bwd_timed when
  * `events` is non-NULL), plus:
  *   dropout_p in [0, 1) (FA_ERR_UNSUPPORTED otherwise; p = 0 is plain attention);
  *   seed, offset: the random stream.  Mask of head bh = b * H + h: Philox4x32-10 (Salmon,
  *     Moraes, Dror, Shaw, SC 2011) with counter (j >> 2, i >> 2, bh, offset) and key (seed
  *     mod 2^32, seed >> 32); element (query i, key j) reads byte (j & 3) of output word
  *     (i & 3) and is kept iff that byte >= round(256 dropout_p).
- * O = (P o Z) V with Z = keep / (1 - p); lse is the logsumexp of the undropped scores.  The
+ * An element is kept with probability (256 - t) / 256, t = round(256 dropout_p), and kept
+ * values are scaled by 256 / (256 - t) (0 if t = 256), so the keep factor Z has mean 1.
+ * O = (P o Z) V; lse is the logsumexp of the undropped scores.  The
  * backward pass regenerates the same mask from (seed, offset): dV = (P o Z)^T dout,
  * dS = P o (Z o (dout V^T) - D).  Pass the forward's seed and offset to the backward.
  * bf16 only (FA_ERR_UNSUPPORTED for FA_F32).
@@ -177,10 +189,11 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_de
  */
 int fa_softmax_rows(const void* x, void* y, float* lse, long long rows, int cols, int dtype, void* stream);
 
-/* A static, never-NULL description of a status code (unknown codes included). */
+/* A static, never-NULL description of a status code (unknown codes included).  Plumbing:
+ * no page defines it. */
 const char* fa_status_string(int status);
 
-/* FA_VERSION of the built library. */
+/* FA_VERSION of the built library.  Plumbing: no page defines it. */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY (same rule as ``oracle.attention``: only tests, the smo
 and the bench's CPU baseline may use it; the HIP library never does, and this module
 imports nothing from it).
 
-"How FlashAttention Actually Works" -- "Why Attention Is Slow" lists dropout among the
-steps of standard attention (matmul, mask, softmax, dropout, matmul) that a fused kernel
-runs on chip.  The pages define neither the random numbers nor where the mask applies;
+"How FlashAttention Actually Works" -- "The GPU Memory Wall: HBM vs. SRAM" lists dropout
+among the steps of standard attention (matmul, mask, softmax, dropout, matmul) that a fused
+kernel runs on chip.  The pages define neither the random numbers nor where the mask applies;
 this module fixes them (readings listed in the design doc):
 
   * Random numbers: Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
@@ -19,7 +19,10 @@ this module fixes them (readings listed in the design doc):
     (j >> 2, i >> 2, bh, offset) and key (seed mod 2^32, seed >> 32) covers the 4 x 4 block
     of (query, key) pairs; element (i, j) reads byte (j & 3) of output word (i & 3) as an
     8-bit integer u and is kept iff u >= t, t = round(256 p) clamped to [0, 256].
-  * Where it applies: O = (P o Z) V with Z = keep / (1 - p); lse stays the logsumexp of
+  * Keep scale: an element is kept with probability (256 - t) / 256 exactly, so kept values
+    are scaled by s = 256 / (256 - t) (s = 0 when t = 256 and nothing is kept), which makes
+    E[Z] = 1 exactly (inverted dropout); 1 / (1 - p) would be biased by the rounding of t.
+  * Where it applies: O = (P o Z) V with Z = keep * s; lse stays the logsumexp of
     the undropped scores (the softmax is not renormalised after dropout).  Gradients of
     L = sum(O * dO) then follow with dP = Z o (dO V^T): dV = (P o Z)^T dO,
     D_i = sum_j P_ij dP_ij = rowsum(dO * O)_i, dS = P o (dP - D), dQ = scale dS K,
@@ -31,7 +34,7 @@ import numpy as np
 
 from .attention import probabilities
 
-__all__ = ["philox4x32_10", "keep_mask", "forward_dropout", "backward_dropout"]
+__all__ = ["philox4x32_10", "keep_mask", "keep_scale", "forward_dropout", "backward_dropout"]
 
 _M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
 _W0, _W1 = np.uint32(0x9E3779B9), np.uint32(0xBB67AE85)
@@ -60,6 +63,13 @@ def threshold(p: float) -> int:
     return int(min(256, max(0, int(np.floor(256.0 * float(p) + 0.5)))))
 
 
+def keep_scale(p: float) -> float:
+    """The factor s of kept values: the reciprocal of the exact keep probability (256 - t) / 256
+    of the 8-bit threshold t, or 0 when t = 256 (nothing is kept)."""
+    t = threshold(p)
+    return 0.0 if t == 256 else 256.0 / (256 - t)
+
+
 def keep_mask(bh: int, n_q: int, n_k: int, p: float, seed: int, offset: int) -> np.ndarray:
     """Boolean [n_q, n_k] keep mask of head bh (see the module docstring)."""
     i = np.arange(n_q)[:, None]
@@ -83,7 +93,7 @@ def forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, of
     for b in range(B):
         for h in range(H):
             pr, m, l = probabilities(q[b, h], k[b, h], scale, causal)
-            z = keep_mask(bh0 + b * H + h, N, N, p, seed, offset) / (1.0 - p)
+            z = keep_mask(bh0 + b * H + h, N, N, p, seed, offset) * keep_scale(p)
             o[b, h] = (pr * z) @ v[b, h]
             lse[b, h] = m + np.log(l)
     return o, lse
@@ -98,7 +108,7 @@ def backward_dropout(q, k, v, do, scale: float, causal: bool, p: float, seed: in
     for b in range(B):
         for h in range(H):
             pr, _, _ = probabilities(q[b, h], k[b, h], scale, causal)
-            z = keep_mask(bh0 + b * H + h, N, N, p, seed, offset) / (1.0 - p)
+            z = keep_mask(bh0 + b * H + h, N, N, p, seed, offset) * keep_scale(p)
             g = do[b, h]
             dv[b, h] = (pr * z).T @ g
             dp = z * (g @ v[b, h].T)

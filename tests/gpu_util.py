@@ -142,15 +142,15 @@ def fp8_forward_bounds(q, k, v, scale: float, causal: bool, rows=None):
 
 def dropout_conditions(q, k, v, do, scale: float, causal: bool, p: float, seed: int, offset: int, bh: int):
     """Condition sums of the dropout forward and backward products of one head (fp64), as
-    in ``bwd_condition`` with the keep factor Z = keep / (1 - p) included, plus the effect
+    in ``bwd_condition`` with the keep factor Z = keep * keep_scale(p) included, plus the effect
     on dQ and dK of D computed from the bf16-stored O:
     (cond_O, cond_dQ, cond_dK, cond_dV) = (|P Z| |V|, scale |dS| |K|, scale |dS|^T |Q|,
     |P Z|^T |dO|) with dS = P (Z (dO V^T) - D)."""
     from oracle import attention as oracle
-    from oracle.dropout import keep_mask
+    from oracle.dropout import keep_mask, keep_scale
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     pr, _, _ = oracle.probabilities(q, k, scale, causal)
-    z = keep_mask(bh, q.shape[0], k.shape[0], p, seed, offset) / (1.0 - p)
+    z = keep_mask(bh, q.shape[0], k.shape[0], p, seed, offset) * keep_scale(p)
     pz = np.abs(pr * z)
     dp = z * (do @ v.T)
     ds = np.abs(pr * (dp - np.sum(pr * dp, axis=1)[:, None]))

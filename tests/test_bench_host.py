@@ -27,7 +27,12 @@ def test_kernel_units_at_the_bench_workload():
     t = bench.kernel_table("bf16", 4, 32, 8192, 128, True)
     assert t["fwd_bf16_kernel"][1] == pytest.approx(2.199023e12, rel=1e-6)
     assert t["dkdv_bf16_kernel"][1] == 2 * t["fwd_bf16_kernel"][1]
-    assert t["dq_bf16_kernel"][1] == 1.5 * t["fwd_bf16_kernel"][1]
+    # dQ counts only dQ = scale dS K (2 N^2 d per head, causal halved); its recomputed S and
+    # dP are executed flops, reported apart
+    assert t["dq_bf16_kernel"][1] == 0.5 * t["fwd_bf16_kernel"][1]
+    assert bench.EXECUTED_FACTOR["dq_bf16_kernel"] * t["dq_bf16_kernel"][1] == 1.5 * t["fwd_bf16_kernel"][1]
+    # frac at the measured dQ time of 2.889 ms: 1.0995e12 / 2.889e-3 / 2.5e15 = 0.152
+    assert t["dq_bf16_kernel"][1] / 2.889e-3 / 2.5e15 == pytest.approx(0.1522, abs=1e-3)
     rows = 4 * 32 * 8192
     assert t["delta_kernel"][1] == 2 * rows * 128 * 2 + 12 * rows
     f = bench.kernel_table("f32", 2, 1, 512, 64, False)

@@ -210,3 +210,50 @@ def test_dropout_rejects_bad_arguments():
     assert bwd(p=1.5) == -3 and bwd(dtype=0) == -3 and bwd(ws=None) == -5
     events = (ctypes.c_void_p * 4)(P, P, None, P)
     assert bwd(events=events) == -1
+
+
+@pytest.mark.parametrize("kw", [dict(B=1, H=1, N=(1 << 30) + 1), dict(B=1, H=1, N=(1 << 31) - 1),
+                                dict(B=1, H=1, N=1 << 30), dict(B=1, H=1 << 24, N=64),
+                                dict(B=1 << 12, H=1 << 12, N=1), dict(B=2, H=1 << 10, N=1 << 19)])
+def test_sizes_past_the_supported_domain(kw):
+    """N <= FA_MAX_N = 2^30 and B*H*ceil(N/64) <= FA_MAX_TILES = 2^24 - 1 (a dispatch holds
+    fewer than 2^32 work-items); every entry point returns FA_ERR_SHAPE outside, before any
+    launch, and fa_bwd_workspace_size returns 0."""
+    assert call_fwd(**kw) == -2
+    assert call_bwd(**kw) == -2
+    assert call_fp8(**kw) == -2
+    a = dict(GOOD, **kw)
+    assert fa.fa_bwd_workspace_size(a["B"], a["H"], a["N"], 64, 1) == 0
+
+
+@pytest.mark.parametrize("B,H,N", [(1, (1 << 24) - 1, 64), (1, 1, (1 << 30) - 64 * 1024), (1, 1023, 1 << 20),
+                                   (3, 5, 1 << 20)])
+def test_sizes_at_the_edge_of_the_domain(B, H, N):
+    """Just inside both limits the sizes are accepted (the workspace size is their check):
+    tiles = B*H*ceil(N/64) <= 2^24 - 1 and N <= 2^30."""
+    assert B * H * -(-N // 64) <= (1 << 24) - 1
+    assert fa.fa_bwd_workspace_size(B, H, N, 128, 1) == 2 * (-(-B * H * N * 4 // 256) * 256)
+
+
+def test_binding_checks_gradients_and_workspace():
+    """The bindings check every caller-supplied tensor before any library call: gradients of
+    the wrong shape, dtype or layout, and a workspace that is too small, strided or on
+    another device, raise instead of handing the library a bad pointer."""
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    need = fa.fa_bwd_workspace_size(1, 2, 8, 64, fa.FA_BF16)
+    for bwd in (lambda **kw: fa.fa_bwd(q, q, q, q, lse, q, **kw),
+                lambda **kw: fa.fa_bwd_dropout(q, q, q, q, lse, q, 0.1, 1, **kw)):
+        with pytest.raises(ValueError, match="dq"):
+            bwd(dq=torch.zeros(1, 2, 8, 32, dtype=torch.bfloat16))
+        with pytest.raises(TypeError, match="dk"):
+            bwd(dk=torch.zeros(1, 2, 8, 64, dtype=torch.float32))
+        with pytest.raises(ValueError, match="dv"):
+            bwd(dv=torch.zeros(1, 2, 64, 8, dtype=torch.bfloat16).transpose(2, 3))
+        with pytest.raises(ValueError, match="workspace"):
+            bwd(workspace=torch.zeros(need - 1, dtype=torch.uint8))
+        with pytest.raises(ValueError, match="workspace"):
+            bwd(workspace=torch.zeros(2 * need, dtype=torch.uint8)[::2])
+        with pytest.raises(ValueError, match="workspace"):
+            bwd(workspace=torch.zeros(need, dtype=torch.uint8, device="meta"))

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.dropout import threshold
+from oracle.dropout import keep_scale, threshold
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
 
@@ -44,6 +44,20 @@ def test_keep_rate_and_extremes():
     assert threshold(0.3) == 77 and threshold(0.5) == 128
 
 
+@pytest.mark.parametrize("p", [0.0, 0.001, 0.1, 0.2, 0.3, 0.5, 0.9, 0.999])
+def test_keep_factor_has_mean_one_exactly(p):
+    """Over the 256 equally likely byte values u, the keep factor Z = [u >= t] * s has mean
+    exactly 1 whenever anything is kept (inverted dropout with the 8-bit threshold t); at
+    p = 0.1 the factor 1 / (1 - p) would give 0.998."""
+    t = threshold(p)
+    z = np.array([(u >= t) * keep_scale(p) for u in range(256)])
+    if t < 256:
+        assert abs(z.mean() - 1.0) <= 1e-15
+    else:
+        assert not z.any()
+    assert keep_scale(0.1) == 256 / 230 and threshold(0.1) == 26
+
+
 def _case(seed=11, N=24, d=8):
     rng = np.random.default_rng(seed)
     return [rng.standard_normal((1, 2, N, d)) for _ in range(4)]
@@ -62,7 +76,7 @@ def test_p_zero_is_plain_attention(causal):
 
 
 def pin_unbiased(fwd_d):
-    """E[O] over masks equals the undropped O (the 1/(1-p) scale): the mean of 400 seeds is
+    """E[O] over masks equals the undropped O (the keep scale): the mean of 400 seeds is
     within a few standard errors."""
     q, k, v, _ = _case(N=16)
     o_ref, _ = oracle.forward(q, k, v, 0.4, False)
@@ -99,7 +113,7 @@ def test_delta_identity_with_dropout():
     p, seed = 0.3, 77
     o, _ = oracle.forward_dropout(q, k, v, 0.25, True, p, seed)
     pr, _, _ = oracle.probabilities(q[0, 1], k[0, 1], 0.25, True)
-    z = oracle.keep_mask(1, 24, 24, p, seed, 0) / (1 - p)
+    z = oracle.keep_mask(1, 24, 24, p, seed, 0) * keep_scale(p)
     dp = z * (do[0, 1] @ v[0, 1].T)
     np.testing.assert_allclose(np.sum(do[0, 1] * o[0, 1], axis=1), np.sum(pr * dp, axis=1), rtol=1e-12)
 
@@ -124,7 +138,7 @@ def _mutant(mistake):
             for h in range(q.shape[1]):
                 pr, _, _ = oracle.probabilities(q[b, h], k[b, h], scale, causal)
                 z = keep_mask(b * q.shape[1] + h, q.shape[2], q.shape[2], p, seed, offset)
-                z = z if mistake == "no 1/(1-p) scale" else z / (1.0 - p)
+                z = z if mistake == "no keep scale" else z * keep_scale(p)
                 o[b, h] = (pr * z) @ v[b, h]
         return o, None
 
@@ -134,7 +148,7 @@ def _mutant(mistake):
         for b in range(q.shape[0]):
             for h in range(q.shape[1]):
                 pr, _, _ = oracle.probabilities(q[b, h], k[b, h], scale, causal)
-                z = keep_mask(b * q.shape[1] + h, q.shape[2], q.shape[2], p, seed, offset) / (1.0 - p)
+                z = keep_mask(b * q.shape[1] + h, q.shape[2], q.shape[2], p, seed, offset) * keep_scale(p)
                 g = do[b, h]
                 dv[b, h] = (pr if mistake == "dV without the mask" else pr * z).T @ g
                 dp = g @ v[b, h].T
@@ -147,7 +161,7 @@ def _mutant(mistake):
     return fwd_d, bwd_d
 
 
-@pytest.mark.parametrize("mistake", ["no 1/(1-p) scale", "dP without the mask", "dV without the mask", None])
+@pytest.mark.parametrize("mistake", ["no keep scale", "dP without the mask", "dV without the mask", None])
 def test_planted_mistakes_are_caught(mistake):
     fwd_d, bwd_d = _mutant(mistake)
     caught = 0

@@ -4,7 +4,7 @@ Philox4x32-10 mask regenerated on the CPU), through the C ABI.
 Bound per element: 2e-2 + 2^-7 cond (the first-order rounding of the bf16 factor of each
 product, of D taken from the bf16-stored O, and of the bf16 output:
 ``gpu_util.dropout_conditions``); mean-abs <= 2e-3 + 2^-8 mean(cond).  With dropout the
-outputs grow by 1 / (1 - p), so the fixed bounds alone would not be fair bf16 bounds.  p = 0 through these entry points must equal the plain path bit for bit."""
+outputs grow by the keep scale 256 / (256 - round(256 p)), so the fixed bounds alone would not be fair bf16 bounds.  p = 0 through these entry points must equal the plain path bit for bit."""
 import numpy as np
 import pytest
 
