@@ -160,3 +160,54 @@ def dropout_conditions(q, k, v, do, scale: float, causal: bool, p: float, seed: 
     cond_dq = scale * (ds @ np.abs(k) + dd[:, None] * (np.abs(pr) @ np.abs(k)))
     cond_dk = scale * (ds.T @ np.abs(q) + np.abs(pr).T @ (dd[:, None] * np.abs(q)))
     return pz @ np.abs(v), cond_dq, cond_dk, pz.T @ np.abs(do)
+
+
+def host_workers() -> int:
+    """Threads for running the oracle head by head: the host cores this process may use, at
+    most 12 (each thread holds a few N x N fp64 arrays at a time)."""
+    import os
+    return max(1, min(12, len(os.sched_getaffinity(0))))
+
+
+def parity_by_head(label: str, heads, got, ref_fn, dtype: str) -> dict:
+    """Compare every element of several outputs with the oracle, one head at a time.
+
+    ``got`` maps an output name to the GPU result as an fp64 array indexed [b, h, ...];
+    ``ref_fn(b, h)`` returns the oracle's values of head (b, h) as a dict of the same names.
+    The oracle runs in a thread pool (NumPy releases the GIL in its kernels; BLAS is held to
+    one thread per call), so host memory stays bounded by a few heads.  Max-abs and mean-abs
+    are taken over all compared elements of each output and checked against the stated
+    tolerance of ``dtype``."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    heads = list(heads)
+
+    def one(bh):
+        b, h = bh
+        ref = ref_fn(b, h)
+        out = {}
+        for name, r in ref.items():
+            g = np.asarray(got[name][b, h], dtype=np.float64)
+            assert g.shape == r.shape, (name, g.shape, r.shape)
+            d = np.abs(g - r)
+            out[name] = (bool(np.all(np.isfinite(g))), float(d.max()), float(d.sum()), d.size)
+        return out
+
+    with threadpool_limits(1), ThreadPoolExecutor(host_workers()) as ex:
+        results = list(ex.map(one, heads))
+    tol = TOL[dtype]
+    summary = {}
+    for name in results[0]:
+        finite = all(r[name][0] for r in results)
+        mx = max(r[name][1] for r in results)
+        mean = sum(r[name][2] for r in results) / sum(r[name][3] for r in results)
+        summary[name] = (mx, mean)
+        log(f"  {label} {name}: {len(heads)} heads, every element: max-abs {mx:.3e} mean-abs {mean:.3e} "
+            f"(tol {tol['max_abs']:.0e}{'' if tol['mean_abs'] is None else ' / %.0e' % tol['mean_abs']})")
+        assert finite, f"{label} {name}: non-finite output"
+        assert mx <= tol["max_abs"], f"{label} {name}: max-abs {mx:.3e} > {tol['max_abs']:.1e}"
+        if tol["mean_abs"] is not None:
+            assert mean <= tol["mean_abs"], f"{label} {name}: mean-abs {mean:.3e} > {tol['mean_abs']:.1e}"
+    return summary
