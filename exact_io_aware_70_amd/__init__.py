@@ -15,13 +15,15 @@ import ctypes
 import math
 import os
 
-__all__ = ["FAError", "library_path", "load_library", "fa_fwd", "fa_bwd", "fa_bwd_workspace_size",
-           "fa_status_string", "fa_version", "FA_OK", "FA_F32", "FA_BF16", "FA_BWD_LAUNCHES"]
+__all__ = ["FAError", "library_path", "load_library", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_size",
+           "fa_status_string", "fa_version", "FA_OK", "FA_F32", "FA_BF16", "FA_BWD_LAUNCHES",
+           "FA_NOALLOC_SCRATCH_BYTES"]
 
 FA_OK = 0
 FA_F32 = 0
 FA_BF16 = 1
 FA_BWD_LAUNCHES = 3  # kernel launches per fa_bwd call: D, dK/dV, dQ
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # static backward scratch of fa_bwd_noalloc, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -59,6 +61,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_bwd_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp,
                                  ctypes.POINTER(vp)]
     lib.fa_bwd_timed.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
     lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, u64, u32, vp]
     lib.fa_fwd_dropout.restype = i
@@ -213,6 +217,27 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, scale=None, causal=Fa
         where = "fa_bwd_timed"
     if st != FA_OK:
         raise FAError(st, where)
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale=None, causal=False, stream=None):
+    """fa_bwd without a workspace argument, for callers that cannot allocate device memory:
+    the library keeps the workspace in a static per-GPU array (FA_NOALLOC_SCRATCH_BYTES),
+    and calls that overlap on one GPU race.  dq, dk, dv must be passed preallocated; nothing
+    is allocated here or in the library.  Returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, sc, 1 if causal else 0,
+                            _dtype_code(q), _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -55,16 +55,25 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
     return 2 * round_up((size_t)B * H * N * sizeof(float), 256);
 }
 
-static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                      int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                      void* const* events) {
+// Pointer, size and alignment checks of the backward entry points (workspace aside).
+static int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                     int dtype) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
     const int st = check_common(B, H, N, d, scale, dtype);
     if (st != FA_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+static int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                      int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* events) {
+    const int st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
     if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, dtype) || !aligned(workspace, 256))
         return FA_ERR_WORKSPACE;
     float* delta = static_cast<float*>(workspace);
@@ -79,6 +88,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* workspace, size_t workspace_bytes, void* stream) {
     return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace,
                       workspace_bytes, stream, nullptr);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                   void* stream) {
+    const int st = bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
+    if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (fa::scratch_address(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return FA_ERR_HIP;
+    return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, ws,
+                      FA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int fa_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -181,6 +203,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned (lse 4-byte)";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a kernel launch";
+        case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: fa_bwd_noalloc needs more than its static scratch (FA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown fa_status code";
     }
 }

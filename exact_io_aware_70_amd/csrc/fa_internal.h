@@ -84,6 +84,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t st);
 
+// Device address, on the device of `stream` (the current device for a NULL stream), of the
+// library's static backward scratch (fa_noalloc.hip), looked up once per device.
+hipError_t scratch_address(hipStream_t stream, void** out);
+
 // Query tiles per (batch, head) of the forward grid.
 long long fwd_grid_tiles(int N, int dtype);
 

@@ -65,7 +65,8 @@ typedef enum {
     FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128} or unknown dtype */
     FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
     FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than fa_bwd_workspace_size() */
-    FA_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+    FA_ERR_HIP = -6,         /* the HIP runtime rejected a launch */
+    FA_ERR_SCRATCH = -7      /* fa_bwd_noalloc: the sizes need more than the static scratch */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -102,6 +103,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The same arguments, checks, kernels and
+ * results as fa_bwd, without the workspace: it lives in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The call allocates and
+ * frees nothing; its first call on a device looks up that device's copy of the array.
+ * Sizes whose fa_bwd_workspace_size() exceeds FA_NOALLOC_SCRATCH_BYTES (B*H*N above about
+ * 2^21 rows) return FA_ERR_SCRATCH before anything is enqueued.  All calls on one GPU share
+ * its array: calls that overlap on one GPU (concurrent streams, threads) race.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /* Number of kernel launches one fa_bwd call makes (D = rowsum(dout * o), dK/dV, dQ). */
 #define FA_BWD_LAUNCHES 3

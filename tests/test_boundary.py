@@ -34,8 +34,8 @@ def test_header_is_plain_c():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd", "fa_bwd_timed", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string",
-            "fa_version"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc",
+            "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string", "fa_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -48,7 +48,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert fa.fa_version() == 100
     seen = set()
-    for code in [0, -1, -2, -3, -4, -5, -6]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7]:
         s = fa.fa_status_string(code)
         assert s and s not in seen
         seen.add(s)
@@ -257,3 +257,28 @@ def test_binding_checks_gradients_and_workspace():
             bwd(workspace=torch.zeros(2 * need, dtype=torch.uint8)[::2])
         with pytest.raises(ValueError, match="workspace"):
             bwd(workspace=torch.zeros(need, dtype=torch.uint8, device="meta"))
+
+
+def call_bwd_noalloc(ptrs=None, **kw):
+    a = dict(GOOD, **kw)
+    p = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P)
+    p.update(ptrs or {})
+    return fa.load_library().fa_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"],
+                                            p["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                                            a["dtype"], None)
+
+
+def test_bwd_noalloc_rejects_before_any_hip_call():
+    """fa_bwd_noalloc runs fa_bwd's checks, then refuses sizes whose workspace exceeds the
+    static scratch (FA_ERR_SCRATCH), all before touching HIP."""
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    for which in ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"]:
+        assert call_bwd_noalloc(ptrs={which: None}) == -1
+    assert call_bwd_noalloc(N=0) == -2 and call_bwd_noalloc(d=80) == -3
+    assert call_bwd_noalloc(ptrs={"dq": P + 4}) == -4
+    # 2 * round_up(rows * 4, 256) bytes: 2^21 rows fit 16 MiB exactly, one more row does not.
+    assert fa.fa_bwd_workspace_size(1, 512, 4096, 128, 1) == 16 << 20
+    assert fa.fa_bwd_workspace_size(1, 512, 4097, 128, 1) > 16 << 20
+    assert call_bwd_noalloc(B=1, H=512, N=4097, d=128) == -7
+    assert call_bwd_noalloc(B=4, H=32, N=16400, d=128) == -7
+    assert "scratch" in fa.fa_status_string(-7)
