@@ -98,7 +98,11 @@ def is_fp8(workload) -> bool:
 def sources_digest(workload="") -> str:
     """SHA-256 of the kernel sources a workload runs (the counter summaries record it)."""
     h = hashlib.sha256()
-    for path in (SOFTMAX_SOURCES if is_softmax(workload) else FP8_SOURCES if is_fp8(workload) else KERNEL_SOURCES):
+    if is_std(workload):
+        paths = KERNEL_SOURCES + STD_SOURCES_EXTRA
+    else:
+        paths = SOFTMAX_SOURCES if is_softmax(workload) else FP8_SOURCES if is_fp8(workload) else KERNEL_SOURCES
+    for path in paths:
         with open(os.path.join(ROOT, path), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -205,7 +209,7 @@ def summarize_pmc(args):
 
     ff, fw = calib(fetch), calib(write)
     names = ["fwd_bf16_kernel", "fwd_f32_kernel", "delta_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
-             "dq_bf16_kernel", "dq_f32_kernel", "softmax_rows_kernel", "fwd_fp8_kernel"]
+             "dq_bf16_kernel", "dq_f32_kernel", "softmax_rows_kernel", "fwd_fp8_kernel"] + STD_KERNELS
     out = {}
     for short in names:
         fv = [v for (_, n), v in fetch.items() if short in n]
@@ -593,6 +597,147 @@ def bench_softmax(args):
     print(json.dumps(out), flush=True)
 
 
+def is_std(workload) -> bool:
+    return workload.startswith("std_")
+
+
+STD_SOURCES_EXTRA = ["exact_io_aware_70_amd/csrc/fa_std.hip", "exact_io_aware_70_amd/csrc/fa_softmax.hip"]
+
+
+def std_bytes(B, H, N, d, elt=2):
+    """Algorithmic HBM bytes of the standard method per step (the N x N terms counted once per
+    pass the method makes over them; matrices are N x ld, ld = N rounded up to 128):
+    forward  S write, S read + P write (softmax), P read (P V); Q, K, V read, O written, lse;
+    backward P read (dV), dP write, P and dP read + dS write (softmax backward), dS read twice
+    (dQ, dK); Q, K, V, dO read, dQ, dK, dV written."""
+    ld = (N + 127) // 128 * 128
+    nn = B * H * N * ld * elt
+    nd = B * H * N * d * elt
+    fwd = 4 * nn + 4 * nd + 4 * B * H * N
+    bwd = 7 * nn + 7 * nd
+    return fwd, bwd
+
+
+def flash_bytes(B, H, N, d, elt=2):
+    """Algorithmic HBM bytes of the flash path per step: fwd Q, K, V read, O and lse written;
+    bwd Q, K, V, O, dO, lse read, dQ, dK, dV written, D and lse*log2(e) written and read."""
+    nd = B * H * N * d * elt
+    return 4 * nd + 4 * B * H * N, 8 * nd + 20 * B * H * N
+
+
+STD_KERNELS = ["std_scores_kernel", "softmax_rows_kernel", "std_pv_kernel", "std_dv_kernel", "std_dp_kernel",
+               "softmax_grad_rows_kernel", "std_dq_kernel", "std_dk_kernel"]
+
+
+def bench_std(args):
+    """One step = the standard (materialising) forward and backward on the workload's inputs;
+    the flash path runs the same step in the same process for the ratios."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_70_amd as fa
+    import fa_inputs
+
+    base = args.workload[len("std_"):]
+    cfg = fa_inputs.CONFIGS[base]
+    B, H, N, d, causal = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]
+    case = fa_inputs.make_case(B, H, N, d, cfg["dtype"], cfg["seed"], cfg["q_scale"], with_grad=True)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(case[n]["bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+                   for n in ("q", "k", "v", "do"))
+    o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ld = fa.fa_std_ld(N)
+    p = torch.empty((B, H, N, ld), dtype=torch.bfloat16, device=dev)
+    dp = torch.empty_like(p)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d, fa.FA_BF16), dtype=torch.uint8, device=dev)
+    sc = case["scale"]
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib * (1 << 20), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def std_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.fa_std_fwd(q, k, v, o, lse, p, scale=sc, causal=causal, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        fa.fa_std_bwd(q, k, v, do, p, dq, dk, dv, dp, scale=sc, causal=causal, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    def flash_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, scale=sc, causal=causal, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale=sc, causal=causal, workspace=ws, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for ev in events:
+            for e in ev:
+                e.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for ev in events:
+            step(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        f = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
+        b = float(np.mean([ev[1].elapsed_time(ev[2]) for ev in events]))
+        return wall * 1e3 / args.steps, f, b
+
+    std_ms, std_f, std_b = timed(std_step)
+    fl_ms, fl_f, fl_b = timed(flash_step)
+    ff, fb = flops(B, H, N, d, causal)
+    sbf, sbb = std_bytes(B, H, N, d)
+    fbf, fbb = flash_bytes(B, H, N, d)
+    value = (ff + fb) / (std_ms * 1e-3) / 1e12
+    ach = (sbf + sbb) / (std_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s (4*B*H*N^2*d fwd, 10*B*H*N^2*d bwd, causal halved): standard "
+                  "materialising attention",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(std_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, Q x%g)" % cfg["q_scale"],
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "pass": "fwd+bwd", "step_flops": ff + fb, "matrix_ld": ld},
+        "std": {"fwd_ms": round(std_f, 4), "bwd_ms": round(std_b, 4), "fwd_bytes": sbf, "bwd_bytes": sbb,
+                "fwd_hbm_floor_ms": round(sbf / 8e12 * 1e3, 4), "bwd_hbm_floor_ms": round(sbb / 8e12 * 1e3, 4)},
+        "flash": {"fwd_ms": round(fl_f, 4), "bwd_ms": round(fl_b, 4), "step_ms": round(fl_ms, 4),
+                  "fwd_bytes": fbf, "bwd_bytes": fbb},
+        "speedup": {"fwd": round(std_f / fl_f, 3), "bwd": round(std_b / fl_b, 3), "step": round(std_ms / fl_ms, 3)},
+        "kernels": ({n: traffic[n] for n in STD_KERNELS if n in traffic} if traffic else None),
+        "roofline": {"kernel": "standard step (all launches)", "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": (sum(t["bytes"] for t in traffic.values()) if traffic else None),
+                     "launch_ms": round(std_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -608,6 +753,9 @@ def main():
 
     if is_softmax(args.workload):
         bench_softmax(args)
+        return
+    if is_std(args.workload):
+        bench_std(args)
         return
     if is_fp8(args.workload):
         bench_fp8(args)

@@ -17,7 +17,7 @@ import os
 
 __all__ = ["FAError", "library_path", "load_library", "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_workspace_size",
            "fa_status_string", "fa_version", "FA_OK", "FA_F32", "FA_BF16", "FA_BWD_LAUNCHES",
-           "FA_NOALLOC_SCRATCH_BYTES"]
+           "FA_NOALLOC_SCRATCH_BYTES", "fa_std_ld", "fa_std_fwd", "fa_std_bwd"]
 
 FA_OK = 0
 FA_F32 = 0
@@ -73,6 +73,14 @@ def load_library() -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = i
     lib.fa_softmax_rows.argtypes = [vp, vp, vp, ctypes.c_longlong, i, i, vp]
     lib.fa_softmax_rows.restype = i
+    lib.fa_std_ld.argtypes = [i]
+    lib.fa_std_ld.restype = i
+    lib.fa_std_matrix_bytes.argtypes = [i, i, i]
+    lib.fa_std_matrix_bytes.restype = sz
+    lib.fa_std_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_std_fwd.restype = i
+    lib.fa_std_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_std_bwd.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -238,6 +246,66 @@ def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale=None, causal=False, st
                             _dtype_code(q), _stream_handle(stream, dev))
     if st != FA_OK:
         raise FAError(st, "fa_bwd_noalloc")
+    return dq, dk, dv
+
+
+def fa_std_ld(N: int) -> int:
+    """Row stride of the standard path's N x N matrices (N rounded up to 128; 0 if N is out of range)."""
+    return int(load_library().fa_std_ld(N))
+
+
+def fa_std_fwd(q, k, v, o=None, lse=None, p=None, scale=None, causal=False, stream=None):
+    """Standard (materialising) attention forward, bf16: S = scale q k^T is written to HBM,
+    softmaxed in place into P, then o = P v.  Returns (o, lse, p) with p the probability
+    matrix [B, H, N, fa_std_ld(N)] bf16 (padding columns 0), which fa_std_bwd reads."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    ld = fa_std_ld(N)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    p = torch.empty((B, H, N, max(ld, 1)), dtype=q.dtype, device=dev) if p is None else p
+    _check("o", o, (B, H, N, d), q.dtype, dev)
+    _check("lse", lse, (B, H, N), torch.float32, dev)
+    _check("p", p, (B, H, N, ld), q.dtype, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_std_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), p.data_ptr(),
+                        B, H, N, d, sc, 1 if causal else 0, _dtype_code(q), _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_std_fwd")
+    return o, lse, p
+
+
+def fa_std_bwd(q, k, v, do, p, dq=None, dk=None, dv=None, dp=None, scale=None, causal=False, stream=None):
+    """Standard attention backward from the stored P of fa_std_fwd: dP = do v^T is written to
+    ``dp`` (workspace, the shape of p; allocated if None), turned into dS in place, then
+    dq = scale dS k, dk = scale dS^T q, dv = P^T do.  Returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    ld = fa_std_ld(N)
+    _check("p", p, (B, H, N, ld), q.dtype, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dp = torch.empty_like(p) if dp is None else dp
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype, dev)
+    _check("dp", dp, (B, H, N, ld), q.dtype, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib.fa_std_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), p.data_ptr(), dq.data_ptr(),
+                        dk.data_ptr(), dv.data_ptr(), dp.data_ptr(), B, H, N, d, sc, 1 if causal else 0,
+                        _dtype_code(q), _stream_handle(stream, dev))
+    if st != FA_OK:
+        raise FAError(st, "fa_std_bwd")
     return dq, dk, dv
 
 

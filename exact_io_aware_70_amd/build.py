@@ -22,7 +22,8 @@ LIB = os.path.join(HERE, "libfa.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_softmax.hip", "fa_fwd_fp8.hip", "fa_noalloc.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_softmax.hip", "fa_fwd_fp8.hip", "fa_noalloc.hip",
+           "fa_std.hip"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
                 "-Wall", "-Wno-unused-function"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",

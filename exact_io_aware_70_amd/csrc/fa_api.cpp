@@ -194,6 +194,50 @@ int fa_softmax_rows(const void* x, void* y, float* lse, long long rows, int cols
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_std_ld(int N) { return N < 1 || N > FA_STD_MAX_N ? 0 : fa::std_ld(N); }
+
+size_t fa_std_matrix_bytes(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1 || N > FA_STD_MAX_N) return 0;
+    return (size_t)B * H * N * fa::std_ld(N) * 2;
+}
+
+// Checks shared by the standard-attention entry points.
+static int std_check(int B, int H, int N, int d, float scale, int dtype) {
+    const int st = check_common(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (N > FA_STD_MAX_N) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* p, int B, int H, int N,
+               int d, float scale, int causal, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse || !p) return FA_ERR_NULL;
+    const int st = std_check(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(p, 16) ||
+        !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    fa::StdArgs a{q, k, v, nullptr, o, p, nullptr, lse, nullptr, nullptr, nullptr, B, H, N, d, scale,
+                  causal ? 1 : 0};
+    const hipError_t e = fa::launch_std_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_std_bwd(const void* q, const void* k, const void* v, const void* dout, const void* p, void* dq, void* dk,
+               void* dv, void* dp, int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+    if (!q || !k || !v || !dout || !p || !dq || !dk || !dv || !dp) return FA_ERR_NULL;
+    const int st = std_check(B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(p, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dp, 16))
+        return FA_ERR_ALIGN;
+    fa::StdArgs a{q, k, v, dout, nullptr, const_cast<void*>(p), dp, nullptr, dq, dk, dv, B, H, N, d, scale,
+                  causal ? 1 : 0};
+    const hipError_t e = fa::launch_std_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK: success";

@@ -77,12 +77,36 @@ struct SoftmaxArgs {
     int dtype;
 };
 
+// Standard (materialising) attention, bf16: p (and dp) are [B, H, N, std_ld(N)] matrices.
+struct StdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;  // backward input
+    void* o;           // forward output
+    void* p;           // forward: written (scores, then probabilities); backward: read
+    void* dp;          // backward: dP, then dS in place
+    float* lse;        // forward output
+    void* dq;          // backward outputs
+    void* dk;
+    void* dv;
+    int B, H, N, d;
+    float scale;
+    int causal;
+};
+
 // Enqueue the forward / backward / row-softmax kernels on `st`; return hipGetLastError()
 // of the launches.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t st);
+// y <- P o (y - rowsum(P o y)) for P = x (bf16 only; lse unused).
+hipError_t launch_softmax_grad(const SoftmaxArgs& a, hipStream_t st);
+hipError_t launch_std_fwd(const StdArgs& a, hipStream_t st);
+hipError_t launch_std_bwd(const StdArgs& a, hipStream_t st);
+// Row stride (elements) of the standard path's N x N matrices: N rounded up to 128.
+int std_ld(int N);
 
 // Device address, on the device of `stream` (the current device for a NULL stream), of the
 // library's static backward scratch (fa_noalloc.hip), looked up once per device.

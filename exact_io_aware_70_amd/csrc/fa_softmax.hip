@@ -282,6 +282,69 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(const T* __restrict__
     }
 }
 
+// Backward of the row softmax (the standard-attention baseline's dS step): with P = softmax
+// rows in x and the upstream gradient dP in y, D = rowsum(P o dP) and y <- P o (dP - D), in
+// place.  Same team layout as the forward kernel: rows that fit (STREAM = false) are read once
+// into registers; longer rows are read twice (D, then the outputs).
+template <typename T, int TEAM, int KV, bool STREAM>
+__global__ __launch_bounds__(256) void softmax_grad_rows_kernel(const T* __restrict__ p, T* __restrict__ g,
+                                                                long long row0, long long rows, int cols) {
+    constexpr int VE = Vec16<T>::VE;
+    constexpr int RPW = 256 / TEAM;
+    __shared__ float red[4];
+    const int t = threadIdx.x % TEAM;
+    const long long r = row0 + (long long)blockIdx.x * RPW + threadIdx.x / TEAM;
+    if (r >= rows) return;
+    const Row<T> row(r, cols, rows);
+
+    // D over this lane's vectors (entries outside the row read as -inf in P and are skipped).
+    auto dot = [&](u32x4 wp, u32x4 wg, float acc) {
+        float fp[VE], fg[VE];
+        Vec16<T>::unpack(wp, fp);
+        Vec16<T>::unpack(wg, fg);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            if (fp[e] != -INFINITY) acc = fmaf(fp[e], fg[e], acc);
+        return acc;
+    };
+    auto out = [&](u32x4 wp, u32x4 wg, float dd, float (&f)[VE]) {
+        float fp[VE], fg[VE];
+        Vec16<T>::unpack(wp, fp);
+        Vec16<T>::unpack(wg, fg);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) f[e] = fp[e] * (fg[e] - dd);
+    };
+    u32x4 wp[KV], wg[KV];
+    float dsum = 0.f;
+    for (int c0 = 0; c0 < (STREAM ? row.nv : 1); c0 += KV * TEAM) {
+#pragma unroll
+        for (int j = 0; j < KV; ++j) {
+            const int idx = c0 + t + j * TEAM;
+            if (idx < row.nv) {
+                wp[j] = row.load(p, idx);
+                wg[j] = row.load(g, idx);
+                dsum = dot(wp[j], wg[j], dsum);
+            }
+        }
+    }
+    const float dd = team_sum<TEAM>(dsum, red);
+    for (int c0 = 0; c0 < (STREAM ? row.nv : 1); c0 += KV * TEAM) {
+#pragma unroll
+        for (int j = 0; j < KV; ++j) {
+            const int idx = c0 + t + j * TEAM;
+            if (idx < row.nv) {
+                if constexpr (STREAM) {
+                    wp[j] = row.load(p, idx);
+                    wg[j] = row.load(g, idx);
+                }
+                float f[VE];
+                out(wp[j], wg[j], dd, f);
+                row.store(g, idx, f);
+            }
+        }
+    }
+}
+
 // Launch shape by row length: short rows get one wave each (four rows per workgroup, no
 // barriers); longer rows a whole workgroup holding as few vectors per lane as the row needs
 // (fewer registers, more workgroups per CU, more bytes in flight); rows past 2048 vectors
@@ -316,6 +379,32 @@ hipError_t launch_softmax_t(const SoftmaxArgs& a, hipStream_t st) {
 
 hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t st) {
     return a.dtype == kBF16 ? launch_softmax_t<__bf16>(a, st) : launch_softmax_t<float>(a, st);
+}
+
+namespace {
+template <typename T, int TEAM, int KV, bool STREAM>
+hipError_t launch_grad_shape(const SoftmaxArgs& a, hipStream_t st) {
+    constexpr int RPW = 256 / TEAM;
+    constexpr long long kMaxGrid = 1LL << 22;
+    for (long long r0 = 0; r0 < a.rows; r0 += kMaxGrid * RPW) {
+        const long long grid = min((a.rows - r0 + RPW - 1) / RPW, kMaxGrid);
+        hipLaunchKernelGGL((softmax_grad_rows_kernel<T, TEAM, KV, STREAM>), dim3((unsigned)grid), dim3(256), 0, st,
+                           static_cast<const T*>(a.x), static_cast<T*>(a.y), r0, a.rows, a.cols);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_softmax_grad(const SoftmaxArgs& a, hipStream_t st) {
+    using T = __bf16;
+    const long long nv_max = a.cols / Vec16<T>::VE + 2;
+    if (nv_max <= 64 * 4) return launch_grad_shape<T, 64, 4, false>(a, st);
+    if (nv_max <= 256 * 2) return launch_grad_shape<T, 256, 2, false>(a, st);
+    if (nv_max <= 256 * 4) return launch_grad_shape<T, 256, 4, false>(a, st);
+    if (nv_max <= 256 * 8) return launch_grad_shape<T, 256, 8, false>(a, st);
+    return launch_grad_shape<T, 256, 8, true>(a, st);
 }
 
 }  // namespace fa

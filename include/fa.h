@@ -205,6 +205,34 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_de
  */
 int fa_softmax_rows(const void* x, void* y, float* lse, long long rows, int cols, int dtype, void* stream);
 
+/*
+ * Standard (materialising) attention: the baseline the pages compare FlashAttention with,
+ * on the same device and harness.  "How FlashAttention Actually Works" -- "The GPU Memory
+ * Wall: HBM vs. SRAM": standard attention writes Q K^T to HBM, reads it back for the softmax,
+ * writes the probability matrix, and reads it again to multiply by V; its backward pass reads
+ * the stored probabilities ("The Backward Pass: Recomputation" describes the alternative).
+ * bf16 only (FA_ERR_UNSUPPORTED otherwise), d in {64, 128}, N <= FA_STD_MAX_N.
+ *
+ * The N x N matrices are bf16 [B, H, N, ld] with ld = fa_std_ld(N) (N rounded up to 128;
+ * the padding columns hold 0 in P and dS); fa_std_matrix_bytes() is the size of one.
+ *
+ * fa_std_fwd: writes S = scale q k^T (-inf where masked) into p, turns it into P = softmax(S)
+ *   in place (lse per row), then o = P v.  p is an output the backward pass reads.
+ * fa_std_bwd: from the forward's p: dv = P^T dout; dP = dout v^T into `dp` (caller-owned, of
+ *   fa_std_matrix_bytes()); dS = P o (dP - rowsum(P o dP)) in place; dq = scale dS k;
+ *   dk = scale dS^T q.
+ * Layout, dtype, stream, ownership and error conventions as fa_fwd / fa_bwd; p and dp must be
+ * 16-byte aligned.  Nothing is allocated; all work is enqueued on `stream`.
+ */
+#define FA_STD_MAX_N 65536
+int fa_std_ld(int N);
+size_t fa_std_matrix_bytes(int B, int H, int N);
+int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* p,
+               int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+int fa_std_bwd(const void* q, const void* k, const void* v, const void* dout, const void* p,
+               void* dq, void* dk, void* dv, void* dp, int B, int H, int N, int d, float scale,
+               int causal, int dtype, void* stream);
+
 /* A static, never-NULL description of a status code (unknown codes included).  Plumbing:
  * no page defines it. */
 const char* fa_status_string(int status);

@@ -35,7 +35,7 @@ def test_header_is_plain_c():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"fa_fwd", "fa_fwd_fp8", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd", "fa_bwd_timed", "fa_bwd_noalloc",
-            "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string", "fa_version"} <= set(names)
+            "fa_std_fwd", "fa_std_bwd", "fa_std_ld", "fa_std_matrix_bytes", "fa_bwd_workspace_size", "fa_softmax_rows", "fa_status_string", "fa_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -282,3 +282,24 @@ def test_bwd_noalloc_rejects_before_any_hip_call():
     assert call_bwd_noalloc(B=1, H=512, N=4097, d=128) == -7
     assert call_bwd_noalloc(B=4, H=32, N=16400, d=128) == -7
     assert "scratch" in fa.fa_status_string(-7)
+
+
+def test_std_sizes_and_rejections():
+    """The standard path's matrix layout ([B, H, N, ld], ld = N rounded up to 128) and its
+    argument checks (bf16 only, N <= FA_STD_MAX_N = 65536), before any HIP call."""
+    lib = fa.load_library()
+    assert [fa.fa_std_ld(n) for n in (1, 127, 128, 129, 4096, 65536)] == [128, 128, 128, 256, 4096, 65536]
+    assert fa.fa_std_ld(0) == 0 and fa.fa_std_ld(65537) == 0
+    assert lib.fa_std_matrix_bytes(2, 3, 100) == 2 * 3 * 100 * 128 * 2
+    assert lib.fa_std_matrix_bytes(1, 1, 65537) == 0
+    a = GOOD
+
+    def fwd(dtype=1, N=a["N"], d=a["d"], q=P, p=P):
+        return lib.fa_std_fwd(q, P, P, P, P, p, a["B"], a["H"], N, d, a["scale"], 0, dtype, None)
+
+    def bwd(dtype=1, N=a["N"], d=a["d"], dp=P):
+        return lib.fa_std_bwd(P, P, P, P, P, P, P, P, dp, a["B"], a["H"], N, d, a["scale"], 1, dtype, None)
+    assert fwd(q=None) == -1 and fwd(p=None) == -1 and bwd(dp=None) == -1
+    assert fwd(dtype=0) == -3 and bwd(dtype=0) == -3 and fwd(d=96) == -3
+    assert fwd(N=65537) == -2 and bwd(N=65537) == -2 and fwd(N=0) == -2
+    assert fwd(p=P + 8) == -4 and bwd(dp=P + 2) == -4
