@@ -97,6 +97,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     // lse and D rows of each stage; each 64-lane 4-byte load fills one 64-float row (lanes
     // past the sub-tile read zeros into the unused upper half).
     __shared__ __attribute__((aligned(256))) float LDs[NS][2][64];  // lse2 | D
+    // With dropout the mask needs registers the kernel does not have (at d = 128 two K
+    // fragments were spilled to scratch, and each reload's vmcnt(0) also waited on the ring's
+    // prefetches): the K fragments of the last KSP k-steps live in LDS instead, each lane's own
+    // 16 bytes, read back per use.  12 KiB more per workgroup keeps two workgroups per CU.
+    constexpr int KSP = DROP ? 3 : 0;
+    __shared__ __attribute__((aligned(16))) bf16x8 Ksp[DROP ? NW : 1][DROP ? KSP : 1][64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
@@ -117,6 +123,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         }
     }
     wait_vmcnt<0>();
+    if constexpr (DROP) {
+#pragma unroll
+        for (int j = 0; j < KSP; ++j) Ksp[wave][j][lane] = kf[DC - KSP + j];
+    }
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -188,7 +198,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < DC; ++kc) {
-            sacc = mfma_bf16(load_bf16x8(r_lane[kc] + so), kf[kc], sacc);
+            const bf16x8 kop = (kc >= DC - KSP) ? Ksp[wave][max(kc - (DC - KSP), 0)][lane] : kf[kc];
+            sacc = mfma_bf16(load_bf16x8(r_lane[kc] + so), kop, sacc);
             pacc = mfma_bf16(load_bf16x8(r_lane[kc] + so + DO_OFF), vf[kc], pacc);
         }
         // P first: the dV products need only P, so the scheduler can run them on the MFMA
