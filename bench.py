@@ -309,6 +309,9 @@ def summarize_sq(args):
     lines += [f"    python3 bench.py --summarize-sq {stats_csv} {' '.join(dirs)} --workload {args.workload}", "",
               "Counter values are means per dispatch (one warm-up and one timed step).  Durations come from "
               "the kernel-trace statistics named above.", ""]
+    if not is_fp8(args.workload):
+        lines += ["The dQ kernel's algorithmic work is the one product dQ = scale dS K; it also recomputes S and dP "
+                  "(the price of a backward without atomics), hence about 3 MFMA instructions per algorithmic one.", ""]
     if is_fp8(args.workload):
         lines += ["The FP8 kernel issues 9 MFMAs per 8 of the attention products (the ninth, with an all-ones "
                   "operand, sums the rounded probabilities), hence about 1.13 MFMA instructions per algorithmic one.",

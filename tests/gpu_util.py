@@ -266,3 +266,29 @@ def std_backward_condition(q, k, v, do, scale: float, causal: bool):
     c = a * np.abs(dp - dd) + p * (np.abs(dp) + e) + np.abs(ds)
     w = c + np.abs(ds)
     return scale * (w @ np.abs(k)), scale * (w.T @ np.abs(q)), (a + p).T @ np.abs(do)
+
+
+def bwd_condition_full(q, k, v, do, scale: float, causal: bool):
+    """Per-element condition sums of the backward for one head (fp64) that also carry what the
+    backward inherits from the forward, each rounding moving a value x by at most BF16_U |x|:
+      * lse: the forward's row sum adds up the bf16-rounded probabilities, so lse is off by at
+        most BF16_U and the recomputed P_ij by at most BF16_U P_ij;
+      * D = rowsum(dO * O) from the bf16-stored O, itself off by the forward's rounding of P
+        before P V and of its output: |dD_i| <= BF16_U e_i,
+        e_i = sum_c |dO_ic| (2 |O_ic| + (P |V|)_ic);
+      * dS = P (dP - D) rounded to bf16: it moves by BF16_U c_ij, c_ij = 2 |dS_ij| + P_ij e_i;
+      * dQ = scale dS K and dK = scale dS^T Q, stored in bf16: moved by
+        BF16_U scale sum (c + |dS|) |K| (and alike for dK);
+      * dV = P^T dO with P off by the lse error and rounded before the product, stored in bf16:
+        moved by BF16_U 3 (P^T |dO|).
+    Returns (cond_dQ, cond_dK, cond_dV), each [N, d]: the bound is 2e-2 + BF16_U * cond."""
+    from oracle import attention as oracle
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    p, _, _ = oracle.probabilities(q, k, scale, causal)
+    o = p @ v
+    dp = do @ v.T
+    dd = np.sum(p * dp, axis=1, keepdims=True)
+    ds = np.abs(p * (dp - dd))
+    e = np.sum(np.abs(do) * (2.0 * np.abs(o) + p @ np.abs(v)), axis=1, keepdims=True)
+    w = 3.0 * ds + p * e
+    return scale * (w @ np.abs(k)), scale * (w.T @ np.abs(q)), 3.0 * (p.T @ np.abs(do))

@@ -7,7 +7,8 @@ import pytest
 
 import fa_inputs
 import oracle
-from tests.gpu_util import assert_parity, bwd_condition, gpu_available, log, parity_by_head, to_device, to_f64
+from tests.gpu_util import (assert_parity, bwd_condition_full, gpu_available, log, parity_by_head, to_device,
+                            to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -106,36 +107,33 @@ def test_bwd_timed_matches_untimed():
     assert all(t > 0 for t in times)
 
 
-def test_bwd_bench_workload_sampled_heads():
-    """The bench's timed step at full size (B=4 H=32 N=8192 d=128, causal, Q drawn x3):
-    every output of three sampled heads against the fp64 oracle, invariants on all heads.
+def test_bwd_bench_workload_all_heads():
+    """The bench's timed step at full size (B=4 H=32 N=8192 d=128, causal, Q drawn x3): every
+    element of dQ, dK and dV of all 128 heads against the fp64 oracle.
 
     With Q drawn x3, |dK| reaches ~11, where storing a value in bf16 alone moves it by up to
-    1/32 (> 2e-2).  The element-wise bound is therefore 2e-2 + 2^-7 cond, with cond the
-    condition sum of each gradient product (``bwd_condition``): the first-order effect of
-    rounding dS (or P) to bf16 before the product and of the bf16 output.  The mean-abs
-    bound stays 2e-3."""
+    1/32 (> 2e-2).  The element-wise bound is therefore 2e-2 + 2^-8 cond, with cond the
+    first-order effect of every rounding the backward depends on (``bwd_condition_full``): dS
+    (or P) rounded to bf16 before the product, the bf16 output, and what it inherits from the
+    forward, the lse of the bf16-rounded row sums and D from the bf16-stored O.  (A bound
+    without the inherited terms held on three sampled heads but not on all 128: dK reached
+    7.0e-2.)  The mean-abs bound stays 2e-3."""
     import torch
     name = "fwd_bf16_causal_b4h32_n8192_d128"
     cfg = fa_inputs.CONFIGS[name]
-    log(f"[bwd] bench workload {name} (fwd + bwd, sampled heads)")
+    log(f"[bwd] bench workload {name} (fwd + bwd, all heads)")
     case = fa_inputs.make_case(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["dtype"], cfg["seed"], cfg["q_scale"],
                                with_grad=True)
     dq, dk, dv = run_bwd(case, True)
-    for (b, h) in [(0, 0), (2, 17), (3, 31)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.backward(case["q"]["values"][sl], case["k"]["values"][sl], case["v"]["values"][sl],
-                              case["do"]["values"][sl], case["scale"], True)
-        conds = bwd_condition(case["q"]["values"][b, h], case["k"]["values"][b, h], case["v"]["values"][b, h],
-                              case["do"]["values"][b, h], case["scale"], True)
-        log(f" head b={b} h={h}")
-        for nm, got, r, c in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref, conds):
-            assert_parity(nm, to_f64(got[sl]), r, "bf16", cond=c)
-    dv_sum = dv.double().sum(dim=2).cpu().numpy()
-    do_sum = case["do"]["values"].astype(np.float64).sum(axis=2)
-    dk_sum = dk.double().sum(dim=2).cpu().numpy()
-    log(f"  sum dV vs sum dO: {np.abs(dv_sum - do_sum).max():.3e}; |sum dK| max {np.abs(dk_sum).max():.3e}")
-    assert np.abs(dv_sum - do_sum).max() <= 2e-2 * max(1.0, np.abs(do_sum).max()) and np.abs(dk_sum).max() < 1.0
-    assert bool(dq.isfinite().all() and dk.isfinite().all() and dv.isfinite().all())
-    del case
+    got = {"dQ": to_f64(dq), "dK": to_f64(dk), "dV": to_f64(dv)}
+    del dq, dk, dv
     torch.cuda.empty_cache()
+    vals = [case[n]["values"] for n in ("q", "k", "v", "do")]
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        r = oracle.backward(*(x[sl] for x in vals), case["scale"], True)
+        c = bwd_condition_full(*(x[b, h] for x in vals), case["scale"], True)
+        return {"dQ": (r[0][0, 0], c[0]), "dK": (r[1][0, 0], c[1]), "dV": (r[2][0, 0], c[2])}
+    parity_by_head("bench workload bwd", [(b, h) for b in range(cfg["B"]) for h in range(cfg["H"])], got, ref,
+                   "bf16")

@@ -94,3 +94,41 @@ def test_std_backward_rounds_more_than_the_flash_arithmetic():
     _, dq, _, _ = _std_emulated(q, k, v, do, scale, True)
     flash_dq = _emulated_grads(q, k, v, do, scale, True)[0]
     assert np.max(np.abs(dq - ref[0][0, 0])) > 2 * np.max(np.abs(flash_dq - ref[0][0, 0]))
+
+
+def _emulated_grads_full(q, k, v, do, scale, causal):
+    """The forward's roundings carried into the backward, as the kernels do: lse from the row
+    sum of the bf16-rounded probabilities, O stored in bf16 (from the rounded probabilities),
+    then P recomputed from that lse, D = rowsum(dO * O), dS and P rounded before their
+    products and every output stored in bf16; everything else in fp64."""
+    s = oracle.scores(q, k, scale, causal)
+    m = s.max(axis=1, keepdims=True)
+    pt = _bf16(np.exp(s - m))
+    l = pt.sum(axis=1, keepdims=True)
+    o = _bf16(pt @ v / l)
+    lse = m + np.log(l)
+    p = np.exp(s - lse)
+    dd = np.sum(do * o, axis=1, keepdims=True)
+    ds = _bf16(p * (do @ v.T - dd))
+    return _bf16(scale * ds @ k), _bf16(scale * ds.T @ q), _bf16(_bf16(p).T @ do)
+
+
+def test_full_condition_covers_the_forwards_roundings():
+    """With the lse and O of a bf16 forward feeding the backward (Q drawn x3), the emulated
+    gradients stay inside 2^-8 cond of ``bwd_condition_full`` everywhere, and they break the
+    bound that ignores those inputs (2^-7 of ``bwd_condition``) somewhere: the D and lse terms
+    are needed."""
+    from tests.gpu_util import bwd_condition_full
+    rng = np.random.default_rng(11)
+    n, d, scale = 512, 128, 128 ** -0.5
+    broke_old = False
+    for causal in (True, False):
+        q, k, v, do = (_bf16(rng.standard_normal((n, d)) * s) for s in (3.0, 1.0, 1.0, 1.0))
+        ref = oracle.backward(q[None, None], k[None, None], v[None, None], do[None, None], scale, causal)
+        got = _emulated_grads_full(q, k, v, do, scale, causal)
+        for g, r, c_new, c_old in zip(got, ref, bwd_condition_full(q, k, v, do, scale, causal),
+                                      bwd_condition(q, k, v, do, scale, causal)):
+            err = np.abs(g - r[0, 0])
+            assert np.all(err <= BF16_U * c_new + 1e-12), float(np.max(err - BF16_U * c_new))
+            broke_old |= bool(np.any(err > 2 * BF16_U * c_old + 1e-12))
+    assert broke_old
