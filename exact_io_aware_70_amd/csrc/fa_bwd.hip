@@ -106,7 +106,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nkt, nkt < kPairTilesBelow);
     int bh, kt;                          // causal: low key tiles see the most queries
     tile_order(L, nkt, gridDim.x / nkt, bh, kt);  // scalar results: this kernel has no VGPR to spare
     const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wave, mykey = kw0 + l32;
@@ -369,7 +369,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int q0 = (nqt - 1 - rank) * BM;  // heaviest (causal) tiles first
@@ -557,8 +557,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_f32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nkt, kt = L % nkt;
+    const int L = xcd_order(blockIdx.x, gridDim.x, nkt, nkt < kPairTilesBelow);
+    int bh, kt;
+    tile_order(L, nkt, gridDim.x / nkt, bh, kt);
     const int k0 = kt * BNK, kw0 = k0 + wave * 32, mykey = kw0 + l32;
     const size_t base = (size_t)bh * N * D, rbase = (size_t)bh * N;
 
@@ -643,9 +644,10 @@ __global__ __launch_bounds__(256, 1) void dq_f32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nqt;
-    const int q0 = (nqt - 1 - (L % nqt)) * BM;
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    int bh, rank;
+    tile_order(L, nqt, gridDim.x / nqt, bh, rank);
+    const int q0 = (nqt - 1 - rank) * BM;
     const size_t base = (size_t)bh * N * D;
     const int wq0 = q0 + wave * 32, myq = wq0 + l32;
 

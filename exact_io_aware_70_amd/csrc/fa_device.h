@@ -197,15 +197,23 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
     return (g % 8 == 0) ? (b % 8) * (g / 8) + b / 8 : b;
 }
 
-// Work order over a grid of nheads x ntiles workgroups (logical id L, after xcd_remap); rank 0
+// Work order over a grid of nheads x ntiles workgroups (logical id L, after xcd_order); rank 0
 // is a head's heaviest causal tile.  By default one head at a time, heaviest tile first: the
-// workgroups in flight on an XCD then share one head's K/V (or Q/dO) stream in L2.  With fewer
-// than kPairTilesBelow tiles per head, that order can leave the last head's heaviest tiles starting
-// after nearly everything else (a list-scheduling model of 64 slots per XCD loses up to a
-// third at 32 tiles per head and nothing at 64 or 128).  Heads then go in pairs whose tiles
-// alternate, which removes the tail; it costs L2 reuse (at N = 8192 it raised the forward's
-// HBM bytes from 1.14x to 1.52x the compulsory ones), so it is kept to the short case.  An odd
-// head count leaves the last head on its own.
+// workgroups in flight on an XCD then share one head's K/V (or Q/dO) stream in L2.
+//   * Head counts that do not divide by 8.  The XCD remap hands each XCD a contiguous eighth
+//     of this order, which would end inside a head and give one XCD that head's heaviest
+//     tiles and the next its lightest (a 3:1 split of the work at one head per two XCDs).
+//     Each head is therefore cut into s = 8 / gcd(nheads, 8) parts of equal causal work, so
+//     that every XCD gets whole parts: part j takes, from each run of 2s consecutive ranks,
+//     the j-th and the (2s-1-j)-th (a heavy tile paired with a light one).  Ranks still
+//     fall through each part heaviest first.
+//   * Few tiles per head.  With fewer than kPairTilesBelow tiles per head, one head at a time
+//     can leave the last head's heaviest tiles starting after nearly everything else (a
+//     list-scheduling model of 64 slots per XCD loses up to a third at 32 tiles per head and
+//     nothing at 64 or 128).  Heads then go in pairs whose tiles alternate, which removes
+//     the tail; it costs L2 reuse (at N = 8192 it raised the forward's HBM bytes from 1.14x
+//     to 1.52x the compulsory ones), so it is kept to the short case.  An odd head count
+//     leaves the last head on its own.
 // Both results are uniform and returned through readfirstlane: the integer divisions are
 // expanded on the VALU, and left in VGPRs they turned every address derived from the head
 // into VALU work inside the loops (and cost the 254-VGPR dK/dV kernel a spill).
@@ -213,8 +221,17 @@ constexpr int kPairTilesBelow = 64;
 __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& head, int& rank) {
     int h, r;
     if (ntiles >= kPairTilesBelow) {
-        h = L / ntiles;
-        r = L - h * ntiles;
+        const int s = 8 / min(nheads & -nheads, 8);  // parts per head
+        if (s > 1 && ntiles % (2 * s) == 0) {
+            const int per = ntiles / s;
+            const int part = L / per, i = L - part * per;
+            h = part / s;
+            const int j = part - h * s;
+            r = 2 * s * (i >> 1) + ((i & 1) ? 2 * s - 1 - j : j);
+        } else {
+            h = L / ntiles;
+            r = L - h * ntiles;
+        }
     } else {
         const int pair = L / (2 * ntiles), j = L - pair * 2 * ntiles;
         if (2 * pair + 1 < nheads) {
@@ -227,6 +244,15 @@ __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& h
     }
     head = __builtin_amdgcn_readfirstlane(h);
     rank = __builtin_amdgcn_readfirstlane(r);
+}
+
+// Logical id of workgroup b in a grid of g = nheads x ntiles: the XCD remap, which gives each
+// XCD a contiguous eighth of tile_order's sequence.  Paired heads (fewer than kPairTilesBelow
+// tiles per head) cannot be cut into equal parts that way, so when an eighth is not a whole
+// number of pairs the ids stay as dispatched, which deals every head's tiles round-robin
+// over the XCDs.
+__device__ __forceinline__ int xcd_order(int b, int g, int ntiles, bool paired) {
+    return (!paired || g % (16 * ntiles) == 0) ? xcd_remap(b, g) : b;
 }
 
 }  // namespace fa

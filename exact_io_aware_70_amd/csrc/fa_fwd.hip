@@ -81,7 +81,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int qt = nqt - 1 - rank;  // heaviest (causal) tiles first
@@ -355,9 +355,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / nqt;
-    const int q0 = (nqt - 1 - (L % nqt)) * BM;
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    int bh, rank;
+    tile_order(L, nqt, gridDim.x / nqt, bh, rank);
+    const int q0 = (nqt - 1 - rank) * BM;
     const size_t base = (size_t)bh * N * D;
     const int wq0 = q0 + wave * 32, myq = wq0 + l32;
 

@@ -52,6 +52,23 @@ def test_bwd_odd_head_counts(B, H, causal):
         assert_parity(name, to_f64(got), r, "bf16")
 
 
+def test_bwd_head_parts():
+    """Three heads at 64 key and query tiles each: both backward kernels cut each head into
+    eight parts of equal causal work.  Every element of dQ, dK, dV."""
+    B, H, N = 1, 3, 8192
+    log(f"[bwd] head parts B={B} H={H} N={N}")
+    case = fa_inputs.make_case(B, H, N, 128, "bf16", seed=430, with_grad=True)
+    dq, dk, dv = run_bwd(case, True)
+    got = {"dQ": to_f64(dq), "dK": to_f64(dk), "dV": to_f64(dv)}
+    vals = [case[n]["values"] for n in ("q", "k", "v", "do")]
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        r = oracle.backward(*(x[sl] for x in vals), case["scale"], True)
+        return {"dQ": r[0][0, 0], "dK": r[1][0, 0], "dV": r[2][0, 0]}
+    parity_by_head("bwd head parts", [(0, h) for h in range(H)], got, ref, "bf16")
+
+
 def test_bwd_medium_bf16_causal():
     log("[bwd] bf16 causal d=128 N=1000, 2x3 heads")
     case = fa_inputs.make_case(2, 3, 1000, 128, "bf16", seed=301, with_grad=True)

@@ -51,6 +51,25 @@ def test_fwd_odd_head_counts(B, H, causal):
     check_full(case, causal, f"bf16 B={B} H={H} N=700 causal={causal}")
 
 
+@pytest.mark.parametrize("B,H", [(1, 3), (1, 4), (3, 2)])
+def test_fwd_head_parts(B, H):
+    """Head counts that do not divide by 8, at 64 query tiles per head: the work order cuts
+    each head into 8 / gcd(B*H, 8) parts of equal causal work, one XCD's worth each.  Every
+    element of O and lse, causal, one head of the oracle at a time."""
+    N = 8192
+    case = fa_inputs.make_case(B, H, N, 128, "bf16", seed=320 + 10 * B + H)
+    log(f"[fwd] head parts B={B} H={H} N={N}")
+    _, _, _, o, lse = run_fwd(case, True)
+    got = {"O": to_f64(o), "lse": to_f64(lse)}
+    vals = [case[n]["values"] for n in ("q", "k", "v")]
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        r_o, r_lse = oracle.forward(*(x[sl] for x in vals), case["scale"], True)
+        return {"O": r_o[0, 0], "lse": r_lse[0, 0]}
+    parity_by_head(f"head parts B={B} H={H}", [(b, h) for b in range(B) for h in range(H)], got, ref, "bf16")
+
+
 def test_fwd_large_logits_bf16():
     """Q drawn x3 (logits std ~3) with a long causal row: the online rescale is exercised."""
     case = fa_inputs.make_case(1, 4, 2000, 128, "bf16", seed=77, q_scale=3.0)
