@@ -206,7 +206,7 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 //     Each head is therefore cut into s = 8 / gcd(nheads, 8) parts of equal causal work, so
 //     that every XCD gets whole parts: part j takes, from each run of 2s consecutive ranks,
 //     the j-th and the (2s-1-j)-th (a heavy tile paired with a light one).  Ranks still
-//     fall through each part heaviest first.
+//     fall through each part heaviest first, and an XCD interleaves its parts by rank.
 //   * Few tiles per head.  With fewer than kPairTilesBelow tiles per head, one head at a time
 //     can leave the last head's heaviest tiles starting after nearly everything else (a
 //     list-scheduling model of 64 slots per XCD loses up to a third at 32 tiles per head and
@@ -223,8 +223,12 @@ __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& h
     if (ntiles >= kPairTilesBelow) {
         const int s = 8 / min(nheads & -nheads, 8);  // parts per head
         if (s > 1 && ntiles % (2 * s) == 0) {
-            const int per = ntiles / s;
-            const int part = L / per, i = L - part * per;
+            // An XCD's eighth holds P whole parts; it walks them rank-major (the i-th tile of
+            // each of its parts, then the (i+1)-th), so the heaviest tiles of all its parts
+            // start first instead of those of its last part starting last.
+            const int per = ntiles / s, P = nheads * s / 8;
+            const int x = L / (P * per), loc = L - x * (P * per);
+            const int i = loc / P, part = x * P + (loc - i * P);
             h = part / s;
             const int j = part - h * s;
             r = 2 * s * (i >> 1) + ((i & 1) ? 2 * s - 1 - j : j);
