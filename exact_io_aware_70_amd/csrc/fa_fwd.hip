@@ -29,12 +29,22 @@ namespace {
 // reference point (exact in real arithmetic), and most tiles skip the O rescale.
 constexpr float kRescaleSlack = 8.0f;
 
+// Grids of at most this many 128-row tiles (one round of two workgroups per CU) run with two
+// key groups per tile at d = 128.  Measured: 17-25% faster at 64-512 tiles (causal), slower
+// from 640 tiles up, where the grid already fills the machine.
+constexpr long long kSplitTilesAtMost = 512;
+
 // ------------------------------------------------------------------ bf16, MFMA 32x32x16
 // Workgroup: NW waves, each owning QB blocks of 32 query rows (every K/V operand read from
 // LDS feeds QB MFMAs).  K/V stream in sub-tiles of 32 keys through an NS-stage
 // LDS ring filled by buffer loads that write LDS directly (no register staging).  Rows of
 // a stage are stored with their 16-byte chunks XOR-swizzled by swz_row(row) (fa_device.h),
 // which keeps both the row-wise K reads and the transposed V reads free of bank conflicts.
+//
+// Key groups (NG = 2, chosen for grids that do not fill the machine): the workgroup has two
+// groups of NW waves over the same query rows; group g walks the sub-tiles 2i + g through a
+// ring of its own, and the groups' partial (m, l, O) merge at the end.  The heaviest causal
+// tiles, whose walk sets the time of a small grid, then take half as long.
 //
 // Software pipeline per sub-tile i (one barrier each):
 //   exponentials of S(i) on the VALU  ||  S(i+1) = K(i+1) Q^T on the MFMA
@@ -56,8 +66,8 @@ struct FwdTile {
 template <int D, bool DROP>
 struct FwdWaves : std::integral_constant<int, D == 64 ? (DROP ? 3 : 4) : 2> {};
 
-template <int D, int NW, int QB, bool CAUSAL, bool DROP>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
+template <int D, int NW, int QB, bool CAUSAL, bool DROP, int NG>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
                                amdgpu_waves_per_eu(FwdWaves<D, DROP>::value, FwdWaves<D, DROP>::value))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, DropoutArgs drop) {
@@ -65,21 +75,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     constexpr int BK = T::BK, NS = T::NS, CPR = T::CPR, STAGE = T::STAGE;
     constexpr int RW = 32 * QB;         // query rows per wave
     constexpr int BM = RW * NW;         // query rows per workgroup
-    constexpr int NT = NW * 64;         // threads
+    constexpr int NT = NG * NW * 64;    // threads
     constexpr int DC = D / 16;          // k-steps of the S^T product
     constexpr int DB = D / 32;          // 32-row blocks of O^T
     constexpr int LPT = BK * CPR / NT;  // LDS-direct loads per thread per tensor per sub-tile
-    constexpr int LPS = 2 * LPT;        // ... for K and V together
+    constexpr int LPS = 2 * NG * LPT;   // ... for K and V of every group's sub-tile
     static_assert(LPT >= 1 && BK * CPR % NT == 0, "tile / thread mismatch");
     static_assert(NS >= 3 && (NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][STAGE];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs[NS][STAGE];
+    static_assert(NG == 1 || NG == 2, "one or two key groups");
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks[NG][NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs[NG][NS][STAGE];
 
     // The wave index is uniform across the wave; readfirstlane lets the compiler see that, so
     // every per-wave decision below is a scalar branch rather than an exec-masked one.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
+    // Key groups: with NG = 2 the waves come in two groups of NW that own the same query rows;
+    // group g takes the sub-tiles t = 2i + g, and the two partial results merge at the end.
+    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave / NW);
+    const int wr = NG == 1 ? wave : wave - grp * NW;  // row block of this wave
 
     const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
     int bh, rank;
@@ -87,7 +102,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     const int qt = nqt - 1 - rank;  // heaviest (causal) tiles first
     const int q0 = qt * BM;
     const size_t base = (size_t)bh * N * D;
-    const int wq0 = q0 + wave * RW;      // first query row of this wave
+    const int wq0 = q0 + wr * RW;        // first query row of this wave
 
     // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop.  Rows past N
     // read row N - 1: finite values whose results are never stored.
@@ -105,7 +120,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int nt = (kv_end + BK - 1) / BK;
     // Sub-tiles this wave computes: causal waves stop at their own last row.
-    const int wave_nt = (wq0 >= N) ? 0 : (CAUSAL ? min(nt, (wq0 + RW - 1) / BK + 1) : nt);
+    const int nsteps = (nt + NG - 1) / NG;  // steps of the workgroup; step i takes sub-tile NG i + g
+    // Steps this wave computes: causal waves stop at their own last row.
+    const int wave_last = (wq0 >= N) ? -1 : (CAUSAL ? min(nt, (wq0 + RW - 1) / BK + 1) : nt) - 1;
+    const int wave_nt = wave_last < grp ? 0 : (wave_last - grp) / NG + 1;
 
     // Per-thread byte offsets of the LDS-direct loads inside one sub-tile (fixed across tiles):
     // LDS chunk g = j * NT + tid holds row g / CPR, logical chunk (g % CPR) ^ swz_row(row).
@@ -118,18 +136,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     const __bf16* Kh = K + base;
     const __bf16* Vh = V + base;
     // Enqueue sub-tile t into stage t % NS (= ST).  Tiles at or past N read zeros.
-    auto issue = [&](auto st, int t) {
+    auto issue = [&](auto st, int i) {
         constexpr int ST = decltype(st)::value;
-        const int kv0 = t * BK;
-        // Each resource spans only its own sub-tile (at most BK rows), so the 32-bit byte
-        // count cannot wrap however long the sequence is.
-        const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D * 2;
-        const i32x4 rk = make_rsrc(Kh + (size_t)min(kv0, N) * D, bytes);
-        const i32x4 rv = make_rsrc(Vh + (size_t)min(kv0, N) * D, bytes);
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            load_lds_b128(rk, lds_addr(&Ks[ST][(j * NT + wave * 64) * 8]), voff[j]);
-            load_lds_b128(rv, lds_addr(&Vs[ST][(j * NT + wave * 64) * 8]), voff[j]);
+        for (int g = 0; g < NG; ++g) {
+            const int kv0 = (NG * i + g) * BK;
+            // Each resource spans only its own sub-tile (at most BK rows), so the 32-bit byte
+            // count cannot wrap however long the sequence is.
+            const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D * 2;
+            const i32x4 rk = make_rsrc(Kh + (size_t)min(kv0, N) * D, bytes);
+            const i32x4 rv = make_rsrc(Vh + (size_t)min(kv0, N) * D, bytes);
+#pragma unroll
+            for (int j = 0; j < LPT; ++j) {
+                load_lds_b128(rk, lds_addr(&Ks[g][ST][(j * NT + wave * 64) * 8]), voff[j]);
+                load_lds_b128(rv, lds_addr(&Vs[g][ST][(j * NT + wave * 64) * 8]), voff[j]);
+            }
         }
     };
 
@@ -149,7 +170,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     // K rows for the A operand of S^T: row l32, chunk 2kc + half (swizzled).
     const __bf16* k_lane[DC];
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) k_lane[kc] = &Ks[0][swz<D>(l32, 16 * kc + 8 * half)];
+    for (int kc = 0; kc < DC; ++kc) k_lane[kc] = &Ks[grp][0][swz<D>(l32, 16 * kc + 8 * half)];
     // Transposed V reads: rows tr_row and tr_row + 8 (16 cc adds whole rows: the swizzle
     // repeats every 16 rows), column 32 db + tr_col.
     const int tr_row = 4 * half + ((lane & 15) >> 2);
@@ -157,8 +178,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
     const __bf16* v_lane[2][DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        v_lane[0][db] = &Vs[0][swz<D>(tr_row, 32 * db + tr_col)];
-        v_lane[1][db] = &Vs[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
+        v_lane[0][db] = &Vs[grp][0][swz<D>(tr_row, 32 * db + tr_col)];
+        v_lane[1][db] = &Vs[grp][0][swz<D>(tr_row + 8, 32 * db + tr_col)];
     }
 
     // S^T of the sub-tile in stage ST for both query blocks: lane = query, register r =
@@ -175,8 +196,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         }
     };
     // Causal (key > query) or tail (key >= N) mask; only sub-tiles that need it call this.
-    auto mask = [&](int t, f32x16 (&s)[QB]) {
-        const int kv0 = t * BK;
+    auto mask = [&](int i, f32x16 (&s)[QB]) {
+        const int kv0 = (NG * i + grp) * BK;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int myq = wq0 + 32 * qb + l32;
@@ -187,7 +208,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
             }
         }
     };
-    auto needs_mask = [&](int t) { return CAUSAL ? (t * BK + BK - 1 > wq0) : (t * BK + BK > N); };
+    auto needs_mask = [&](int i) {
+        const int kv0 = (NG * i + grp) * BK;
+        return CAUSAL ? (kv0 + BK - 1 > wq0) : (kv0 + BK > N);
+    };
     static_assert(BK % 32 == 0, "a sub-tile past the wave's rows must be fully masked");
     static_assert(BK % 16 == 0, "stage bases must keep the 16-row swizzle period");
     // Row max of S(t) and the (rare) raise of the reference max: O and l are rescaled by
@@ -289,7 +313,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 uint32_t m[4];
-                dropout_bytes<true>(drop, (uint32_t)bh, wq0 + 32 * qb + l32, i * BK, lane, m);
+                dropout_bytes<true>(drop, (uint32_t)bh, wq0 + 32 * qb + l32, (NG * i + grp) * BK, lane, m);
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
                     u32x4 w4 = __builtin_bit_cast(u32x4, pb[qb][cc]);
@@ -306,16 +330,53 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         raise_ref(nxt);
     };
     int i = 0;
-    for (; i + 3 < nt; i += 4) {
+    for (; i + 3 < nsteps; i += 4) {
         step(S0{}, i, sa, sb);
         step(S1{}, i + 1, sb, sa);
         step(S2{}, i + 2, sa, sb);
         step(S3{}, i + 3, sb, sa);
     }
-    if (i < nt) step(S0{}, i, sa, sb);
-    if (i + 1 < nt) step(S1{}, i + 1, sb, sa);
-    if (i + 2 < nt) step(S2{}, i + 2, sa, sb);
+    if (i < nsteps) step(S0{}, i, sa, sb);
+    if (i + 1 < nsteps) step(S1{}, i + 1, sb, sa);
+    if (i + 2 < nsteps) step(S2{}, i + 2, sa, sb);
     wait_vmcnt<0>();  // no LDS-direct load may still be writing when the workgroup's LDS is freed
+
+    if constexpr (NG == 2) {
+        // Merge the two groups' partial results of each row ("How does FlashAttention optimize
+        // memory and speed via tiling?", Core Technical Innovations, item 2): with m = max(m0, m1),
+        // O = 2^(m0 - m) O0 + 2^(m1 - m) O1 and l likewise.  Group 1 hands its (m, l, O) over
+        // through the LDS of the finished rings, laid out [row block][value][lane].
+        constexpr int NV = QB * DB * 16 + 2 * QB;  // values per lane
+        static_assert(NW * NV * 64 * 4 <= (int)(sizeof(Ks) + sizeof(Vs)), "merge buffer");
+        float* xs = reinterpret_cast<float*>(&Ks[0][0][0]) + wr * NV * 64 + lane;
+        __syncthreads();  // every wave is done with the rings
+        if (grp == 1) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) xs[((qb * DB + db) * 16 + r) * 64] = oacc[qb][db][r];
+                xs[(QB * DB * 16 + qb) * 64] = m_ref[qb];
+                xs[(QB * DB * 16 + QB + qb) * 64] = lsum[qb];
+            }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float m1 = xs[(QB * DB * 16 + qb) * 64], l1 = xs[(QB * DB * 16 + QB + qb) * 64];
+            const float mn = fmaxf(m_ref[qb], m1);
+            const float a0 = fast_exp2(m_ref[qb] - mn), a1 = fast_exp2(m1 - mn);
+            lsum[qb] = lsum[qb] * a0 + l1 * a1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[qb][db][r] = oacc[qb][db][r] * a0 + xs[((qb * DB + db) * 16 + r) * 64] * a1;
+            m_ref[qb] = mn;
+        }
+    }
 
     // Epilogue: O = acc / l, lse = m_ref ln 2 + ln l.
 #pragma unroll
@@ -457,17 +518,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
     }
 }
 
-template <int D, int NW, int QB, bool CAUSAL>
+template <int D, int NW, int QB, bool CAUSAL, int NG>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t st) {
     constexpr int BM = 32 * QB * NW;
     const int nqt = (a.N + BM - 1) / BM;
     const long long grid = (long long)nqt * a.B * a.H;
     if (a.dropout)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL, true>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL, true, NG>), dim3((unsigned)grid), dim3(NG * NW * 64), 0, st,
                            (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
                            a.N, nqt, a.scale * kLog2e, a.drop);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL, false>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL, false, NG>), dim3((unsigned)grid), dim3(NG * NW * 64), 0, st,
                            (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
                            a.N, nqt, a.scale * kLog2e, a.drop);
     return hipGetLastError();
@@ -487,8 +548,15 @@ hipError_t launch_f32(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     if (a.dtype == kBF16) {
-        if (a.d == 128) return a.causal ? launch_bf16<128, 4, 1, true>(a, st) : launch_bf16<128, 4, 1, false>(a, st);
-        return a.causal ? launch_bf16<64, 4, 1, true>(a, st) : launch_bf16<64, 4, 1, false>(a, st);
+        if (a.d == 128) {
+            // Grids that do not fill the machine twice over: each tile's keys split over two
+            // groups of waves, which halves the walk of the heaviest causal tiles.
+            const long long tiles = (long long)((a.N + 127) / 128) * a.B * a.H;
+            if (tiles <= kSplitTilesAtMost)
+                return a.causal ? launch_bf16<128, 4, 1, true, 2>(a, st) : launch_bf16<128, 4, 1, false, 2>(a, st);
+            return a.causal ? launch_bf16<128, 4, 1, true, 1>(a, st) : launch_bf16<128, 4, 1, false, 1>(a, st);
+        }
+        return a.causal ? launch_bf16<64, 4, 1, true, 1>(a, st) : launch_bf16<64, 4, 1, false, 1>(a, st);
     }
     if (a.d == 128) return a.causal ? launch_f32<128, true>(a, st) : launch_f32<128, false>(a, st);
     return a.causal ? launch_f32<64, true>(a, st) : launch_f32<64, false>(a, st);

@@ -32,9 +32,8 @@
  *     rounded to the input dtype (round to nearest even).  The fp32 path uses fp32
  *     MFMA throughout.
  *   - Supported: B, H, N >= 1; N <= FA_MAX_N (2^30); d in {64, 128};
- *     B*H*ceil(N/64) <= FA_MAX_TILES (2^24 - 1: every attention launch is one 256-thread
- *     workgroup per tile of at least 64 rows, and a dispatch holds fewer than 2^32
- *     work-items).  Sizes outside this return FA_ERR_SHAPE.  Inside it no index or byte
+ *     B*H*ceil(N/64) <= FA_MAX_TILES (2^24 - 1: every attention launch has at most 256
+ *     threads per 64 rows, and a dispatch holds fewer than 2^32 work-items).  Sizes outside this return FA_ERR_SHAPE.  Inside it no index or byte
  *     count wraps: tensor offsets are 64-bit, and each range-checked tile load spans only
  *     its own tile.
  *   (fa_softmax_rows, below, has conventions of its own.)

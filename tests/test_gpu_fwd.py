@@ -70,6 +70,24 @@ def test_fwd_head_parts(B, H):
     parity_by_head(f"head parts B={B} H={H}", [(b, h) for b in range(B) for h in range(H)], got, ref, "bf16")
 
 
+@pytest.mark.parametrize("B,H,N,causal,q_scale", [(1, 2, 8192, True, 3.0), (1, 1, 5000, False, 1.0), (2, 3, 1500, True, 1.0)])
+def test_fwd_key_groups(B, H, N, causal, q_scale):
+    """Grids of at most 512 tiles run with two key groups per tile whose partial (m, l, O)
+    merge on chip; every element of O and lse, including a Q x3 case (rescales in both
+    groups) and ragged lengths."""
+    case = fa_inputs.make_case(B, H, N, 128, "bf16", seed=340 + N + H, q_scale=q_scale)
+    log(f"[fwd] key groups B={B} H={H} N={N} causal={causal} q x{q_scale:g}")
+    _, _, _, o, lse = run_fwd(case, causal)
+    got = {"O": to_f64(o), "lse": to_f64(lse)}
+    vals = [case[n]["values"] for n in ("q", "k", "v")]
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        r_o, r_lse = oracle.forward(*(x[sl] for x in vals), case["scale"], causal)
+        return {"O": r_o[0, 0], "lse": r_lse[0, 0]}
+    parity_by_head(f"key groups B={B} H={H} N={N}", [(b, h) for b in range(B) for h in range(H)], got, ref, "bf16")
+
+
 def test_fwd_large_logits_bf16():
     """Q drawn x3 (logits std ~3) with a long causal row: the online rescale is exercised."""
     case = fa_inputs.make_case(1, 4, 2000, 128, "bf16", seed=77, q_scale=3.0)
