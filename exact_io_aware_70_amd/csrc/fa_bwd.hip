@@ -75,8 +75,11 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
 // rows, and their dS = P (0 - 0) = 0, so they contribute nothing.
 // DROP: dropout (dV takes the dropped P; dS = P (Z dP - D) with Z the keep factor; the
 // keep scale of dV is applied at the store).
-template <int D, int NW, bool CAUSAL, bool DROP>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
+// NG = 2 (grids of at most kSplitTilesAtMost key tiles): two groups of NW waves per key tile
+// take alternate query sub-tiles through rings of their own, so the heaviest key tiles' walk
+// halves; group 1's dK, dV partials join group 0's through the LDS at the end.
+template <int D, int NW, bool CAUSAL, bool DROP, int NG>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2,
@@ -85,31 +88,38 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     constexpr int NS = 4;               // LDS stages
     constexpr int STAGE = BQ * D;       // bf16 elements per tensor per stage
     constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int NT = NW * 64;
+    constexpr int NT = NG * NW * 64;
     constexpr int DC = D / 16, DB = D / 32;
     constexpr int LPT = BQ * CPR / NT;  // LDS-direct 16-byte loads per thread per tensor per sub-tile
-    constexpr int LPS = 2 * LPT + 2;    // per sub-tile: Q, dO, then lse and D (4 bytes per lane)
+    constexpr int LPS = NG * (2 * LPT + 2);  // per step and group: Q, dO, then lse and D (4 bytes per lane)
     static_assert(LPT >= 1 && BQ * CPR % NT == 0, "tile / thread mismatch");
     static_assert((NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(1024))) __bf16 Qs[NS][STAGE];
-    __shared__ __attribute__((aligned(1024))) __bf16 dOs[NS][STAGE];
+    static_assert(NG == 1 || NG == 2, "one or two query groups");
+    __shared__ __attribute__((aligned(1024))) __bf16 Qs[NG][NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 dOs[NG][NS][STAGE];
     // lse and D rows of each stage; each 64-lane 4-byte load fills one 64-float row (lanes
     // past the sub-tile read zeros into the unused upper half).
-    __shared__ __attribute__((aligned(256))) float LDs[NS][2][64];  // lse2 | D
+    __shared__ __attribute__((aligned(256))) float LDs[NG][NS][2][64];  // lse2 | D
     // With dropout the mask needs registers the kernel does not have (at d = 128 two K
     // fragments were spilled to scratch, and each reload's vmcnt(0) also waited on the ring's
     // prefetches): the K fragments of the last KSP k-steps live in LDS instead, each lane's own
     // 16 bytes, read back per use.  12 KiB more per workgroup keeps two workgroups per CU.
-    constexpr int KSP = DROP ? 3 : 0;
-    __shared__ __attribute__((aligned(16))) bf16x8 Ksp[DROP ? NW : 1][DROP ? KSP : 1][64];
+    // The two-group form needs a few registers for its group index and loop bounds: two K
+    // fragments move to LDS there too.
+    constexpr int KSP = DROP ? 3 : (NG == 2 ? 2 : 0);
+    __shared__ __attribute__((aligned(16))) bf16x8 Ksp[KSP ? NG * NW : 1][KSP ? KSP : 1][64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
+    // Query groups (NG = 2): two groups of NW waves own the same keys; group g takes every
+    // other query sub-tile of the ring, and the two partial dK, dV add up at the end.
+    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave / NW);
+    const int wr = NG == 1 ? wave : wave - grp * NW;
     const int L = xcd_order(blockIdx.x, gridDim.x, nkt, nkt < kPairTilesBelow);
     int bh, kt;                          // causal: low key tiles see the most queries
     tile_order(L, nkt, gridDim.x / nkt, bh, kt);  // scalar results: this kernel has no VGPR to spare
-    const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wave, mykey = kw0 + l32;
+    const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wr, mykey = kw0 + l32;
     const size_t base = (size_t)bh * N * D, rbase = (size_t)bh * N;
 
     // K^T and V^T fragments (B operands): row mykey (clamped; results past N are not stored).
@@ -123,7 +133,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         }
     }
     wait_vmcnt<0>();
-    if constexpr (DROP) {
+    if constexpr (KSP > 0) {
 #pragma unroll
         for (int j = 0; j < KSP; ++j) Ksp[wave][j][lane] = kf[DC - KSP + j];
     }
@@ -135,14 +145,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     }
 
     const int t_begin = CAUSAL ? k0 / BQ : 0;   // first query sub-tile any key here can see
-    const int nsteps = (N + BQ - 1) / BQ - t_begin;
+    const int nsub = (N + BQ - 1) / BQ - t_begin;  // query sub-tiles of the ring
+    const int nsteps = (nsub + NG - 1) / NG;         // step i takes sub-tile NG i + g of the ring
     // The ring walks the query sub-tiles from the last one down to t_begin, so the workgroups
     // of a head, which all start at the last sub-tile, read the same Q / dO sub-tile at about
     // the same time and an XCD fetches it from HBM about once.  Walking up from each one's own
     // diagonal, they read different sub-tiles at a time and rely on L2 holding the head's whole
     // Q / dO: at B=4 H=32 N=8192 that fetched 1.42x the compulsory bytes, against 1.19x now.
-    const int t_last = t_begin + nsteps - 1;
-    auto tile_of = [&](int i) { return i < nsteps ? t_last - i : -1; };  // -1: past the end
+    const int t_last = t_begin + nsub - 1;
+    auto tile_of = [&](int i, int g) { return NG * i + g < nsub ? t_last - (NG * i + g) : -1; };  // -1: past the end
     const int wave_first = CAUSAL ? kw0 / BQ : 0;
     const bool wave_live = kw0 < N;
 
@@ -154,36 +165,40 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     }
     // Sub-tile t of the query range into stage ST.  Rows at or past N read zeros.  Every
     // wave writes the (identical) lse / D rows, so each wave issues the same loads.
-    auto issue = [&](auto st, int t) {
+    auto issue = [&](auto st, int i) {
         constexpr int ST = decltype(st)::value;
-        const int q0 = t < 0 ? N : t * BQ;  // past the end: zero rows, the loads read zeros
-        // Each resource spans only this sub-tile (at most BQ rows): the 32-bit byte count
-        // cannot wrap however long the sequence is.
-        const uint32_t rows = (uint32_t)min(max(0, N - q0), BQ);
-        const i32x4 rq = make_rsrc(Q + base + (size_t)min(q0, N) * D, rows * D * 2);
-        const i32x4 ro = make_rsrc(dO + base + (size_t)min(q0, N) * D, rows * D * 2);
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            load_lds_b128(rq, lds_addr(&Qs[ST][(j * NT + wave * 64) * 8]), voff[j]);
-            load_lds_b128(ro, lds_addr(&dOs[ST][(j * NT + wave * 64) * 8]), voff[j]);
+        for (int g = 0; g < NG; ++g) {
+            const int t = tile_of(i, g);
+            const int q0 = t < 0 ? N : t * BQ;  // past the end: zero rows, the loads read zeros
+            // Each resource spans only this sub-tile (at most BQ rows): the 32-bit byte count
+            // cannot wrap however long the sequence is.
+            const uint32_t rows = (uint32_t)min(max(0, N - q0), BQ);
+            const i32x4 rq = make_rsrc(Q + base + (size_t)min(q0, N) * D, rows * D * 2);
+            const i32x4 ro = make_rsrc(dO + base + (size_t)min(q0, N) * D, rows * D * 2);
+#pragma unroll
+            for (int j = 0; j < LPT; ++j) {
+                load_lds_b128(rq, lds_addr(&Qs[g][ST][(j * NT + wave * 64) * 8]), voff[j]);
+                load_lds_b128(ro, lds_addr(&dOs[g][ST][(j * NT + wave * 64) * 8]), voff[j]);
+            }
+            const i32x4 rl = make_rsrc(LSE2 + rbase + min(q0, N), rows * 4);
+            const i32x4 rd = make_rsrc(Delta + rbase + min(q0, N), rows * 4);
+            load_lds_b32(rl, lds_addr(&LDs[g][ST][0][0]), (uint32_t)(lane * 4));
+            load_lds_b32(rd, lds_addr(&LDs[g][ST][1][0]), (uint32_t)(lane * 4));
         }
-        const i32x4 rl = make_rsrc(LSE2 + rbase + min(q0, N), rows * 4);
-        const i32x4 rd = make_rsrc(Delta + rbase + min(q0, N), rows * 4);
-        load_lds_b32(rl, lds_addr(&LDs[ST][0][0]), (uint32_t)(lane * 4));
-        load_lds_b32(rd, lds_addr(&LDs[ST][1][0]), (uint32_t)(lane * 4));
     };
 
     // LDS read addresses that depend only on the lane.
     const __bf16* r_lane[DC];  // Q / dO rows (A operands of S and dP): row l32, chunk 2kc + half
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) r_lane[kc] = &Qs[0][swz<D>(l32, 16 * kc + 8 * half)];
+    for (int kc = 0; kc < DC; ++kc) r_lane[kc] = &Qs[grp][0][swz<D>(l32, 16 * kc + 8 * half)];
     const int tr_row = 4 * half + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const __bf16* t_lane[2][DB];  // transposed reads (dO^T, Q^T): rows tr_row, tr_row + 8
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        t_lane[0][db] = &Qs[0][swz<D>(tr_row, 32 * db + tr_col)];
-        t_lane[1][db] = &Qs[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
+        t_lane[0][db] = &Qs[grp][0][swz<D>(tr_row, 32 * db + tr_col)];
+        t_lane[1][db] = &Qs[grp][0][swz<D>(tr_row + 8, 32 * db + tr_col)];
     }
     constexpr int DO_OFF = (int)(sizeof(Qs) / sizeof(__bf16));  // dOs follows Qs in the same layout
 
@@ -208,8 +223,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         f32x4 d4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&LDs[ls][0][8 * g + 4 * half]);
-            d4[g] = *reinterpret_cast<const f32x4*>(&LDs[ls][1][8 * g + 4 * half]);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&LDs[grp][ls][0][8 * g + 4 * half]);
+            d4[g] = *reinterpret_cast<const f32x4*>(&LDs[grp][ls][1][8 * g + 4 * half]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float p = fast_exp2(fmaf(sacc[4 * g + e], scale_log2, -l4[e]));
@@ -265,8 +280,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
         constexpr int ST = decltype(st)::value;
         wait_vmcnt<(NS - 2) * LPS>();  // sub-tile i has landed (this wave's share) ...
         __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
-        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, tile_of(i + NS - 1));
-        const int t = tile_of(i);
+        issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, i + NS - 1);
+        const int t = tile_of(i, grp);
         if (!wave_live || (CAUSAL ? t <= wave_first : false)) return;
         body(std::false_type{}, ST * STAGE, ST, t * BQ);
     };
@@ -276,9 +291,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
     static_assert(NS == 4, "the loop below is unrolled over four stages");
-    issue(S0{}, tile_of(0));
-    issue(S1{}, tile_of(1));
-    issue(S2{}, tile_of(2));
+    issue(S0{}, 0);
+    issue(S1{}, 1);
+    issue(S2{}, 2);
     int i = 0;
     for (; i + 3 < nsteps; i += 4) {
         step(S0{}, i);
@@ -294,7 +309,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
     if constexpr (CAUSAL) {
         static_assert(NS >= NW, "each wave needs a stage of its own for its diagonal sub-tile");
         __syncthreads();  // ... and every wave is done reading the ring
-        if (wave_live) {
+        if (grp == 0 && wave_live) {
             // The diagonal sub-tile (query rows kw0 .. kw0 + 31) into this wave's own stage;
             // only this wave reads it, so its own vmcnt wait is enough.
             const int q0 = kw0;
@@ -305,16 +320,43 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
             for (int j = 0; j < BQ * CPR / 64; ++j) {
                 const int g = j * 64 + lane, r = g / CPR, c = (g % CPR) ^ swz_row<D>(r);
                 const uint32_t vo = (uint32_t)((r * D + c * 8) * 2);
-                load_lds_b128(rq, lds_addr(&Qs[wave][j * 64 * 8]), vo);
-                load_lds_b128(ro, lds_addr(&dOs[wave][j * 64 * 8]), vo);
+                load_lds_b128(rq, lds_addr(&Qs[0][wr][j * 64 * 8]), vo);
+                load_lds_b128(ro, lds_addr(&dOs[0][wr][j * 64 * 8]), vo);
             }
             const i32x4 rl = make_rsrc(LSE2 + rbase + q0, rows * 4);
             const i32x4 rd = make_rsrc(Delta + rbase + q0, rows * 4);
-            load_lds_b32(rl, lds_addr(&LDs[wave][0][0]), (uint32_t)(lane * 4));
-            load_lds_b32(rd, lds_addr(&LDs[wave][1][0]), (uint32_t)(lane * 4));
+            load_lds_b32(rl, lds_addr(&LDs[0][wr][0][0]), (uint32_t)(lane * 4));
+            load_lds_b32(rd, lds_addr(&LDs[0][wr][1][0]), (uint32_t)(lane * 4));
             wait_vmcnt<0>();
-            body(std::true_type{}, wave * STAGE, wave, kw0);
+            body(std::true_type{}, wr * STAGE, wr, kw0);
         }
+    }
+
+    if constexpr (NG == 2) {
+        // dK and dV are plain sums over queries: group 1's partials join group 0's through the
+        // LDS of the finished rings, laid out [key block][value][lane].
+        constexpr int NV = 2 * DB * 16;
+        static_assert(NW * NV * 64 * 4 <= (int)(sizeof(Qs) + sizeof(dOs)), "merge buffer");
+        float* xs = reinterpret_cast<float*>(&Qs[0][0][0]) + wr * NV * 64 + lane;
+        __syncthreads();  // group 0 is done with its diagonal stages
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    xs[(db * 16 + r) * 64] = dk[db][r];
+                    xs[((DB + db) * 16 + r) * 64] = dv[db][r];
+                }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dk[db][r] += xs[(db * 16 + r) * 64];
+                dv[db][r] += xs[((DB + db) * 16 + r) * 64];
+            }
     }
 
     if (mykey < N) {
@@ -348,33 +390,40 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64), amdgpu_waves_
 // DROP: dropout (dS = P (Z dP - D) with Z the keep factor).
 // Occupancy: two waves per SIMD at d = 128; three at d = 64, where the kernel fits 168 VGPRs
 // (two with dropout, whose mask would spill at that budget).
+// NG = 2 (grids of at most kSplitTilesAtMost query tiles): two groups of NW waves per query
+// tile take alternate key sub-tiles, and group 1's partial dQ joins group 0's at the end.
 template <int D, bool DROP>
 struct DqWaves : std::integral_constant<int, D == 64 && !DROP ? 3 : 2> {};
 
-template <int D, int NW, bool CAUSAL, bool DROP>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
+template <int D, int NW, bool CAUSAL, bool DROP, int NG>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
                                amdgpu_waves_per_eu(DqWaves<D, DROP>::value, DqWaves<D, DROP>::value))) void dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, DropoutArgs drop) {
-    constexpr int BK = 32, NS = 4, STAGE = BK * D, CPR = D / 8, NT = NW * 64;
+    constexpr int BK = 32, NS = 4, STAGE = BK * D, CPR = D / 8, NT = NG * NW * 64;
     constexpr int BM = 32 * NW, DC = D / 16, DB = D / 32;
     constexpr int LPT = BK * CPR / NT;
-    constexpr int LPS = 2 * LPT;
+    constexpr int LPS = 2 * NG * LPT;
     static_assert(LPT >= 1 && BK * CPR % NT == 0, "tile / thread mismatch");
     static_assert((NS - 2) * LPS < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][STAGE];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs[NS][STAGE];
+    static_assert(NG == 1 || NG == 2, "one or two key groups");
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks[NG][NS][STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs[NG][NS][STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
+    // Key groups (NG = 2): two groups of NW waves own the same queries; group g takes the
+    // sub-tiles 2i + g, and the two partial dQ add up at the end.
+    const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave / NW);
+    const int wr = NG == 1 ? wave : wave - grp * NW;
     const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int q0 = (nqt - 1 - rank) * BM;  // heaviest (causal) tiles first
     const size_t base = (size_t)bh * N * D;
-    const int wq0 = q0 + 32 * wave, myq = wq0 + l32;
+    const int wq0 = q0 + 32 * wr, myq = wq0 + l32;
 
     bf16x8 qf[DC], of[DC];
     {
@@ -396,7 +445,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int nt = (kv_end + BK - 1) / BK;
-    const int wave_nt = (wq0 >= N) ? 0 : (CAUSAL ? min(nt, (wq0 + 31) / BK + 1) : nt);
+    const int nsteps = (nt + NG - 1) / NG;  // step i takes sub-tile NG i + g
+    const int wave_last = (wq0 >= N) ? -1 : (CAUSAL ? min(nt, (wq0 + 31) / BK + 1) : nt) - 1;
+    const int wave_nt = wave_last < grp ? 0 : (wave_last - grp) / NG + 1;
 
     uint32_t voff[LPT];
 #pragma unroll
@@ -404,30 +455,33 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         const int g = j * NT + tid, r = g / CPR, c = (g % CPR) ^ swz_row<D>(r);
         voff[j] = (uint32_t)((r * D + c * 8) * 2);
     }
-    auto issue = [&](auto st, int t) {
+    auto issue = [&](auto st, int i) {
         constexpr int ST = decltype(st)::value;
-        const int kv0 = t * BK;
-        const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D * 2;  // one sub-tile: never wraps
-        const i32x4 rk = make_rsrc(K + base + (size_t)min(kv0, N) * D, bytes);
-        const i32x4 rv = make_rsrc(V + base + (size_t)min(kv0, N) * D, bytes);
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            load_lds_b128(rk, lds_addr(&Ks[ST][(j * NT + wave * 64) * 8]), voff[j]);
-            load_lds_b128(rv, lds_addr(&Vs[ST][(j * NT + wave * 64) * 8]), voff[j]);
+        for (int g = 0; g < NG; ++g) {
+            const int kv0 = (NG * i + g) * BK;
+            const uint32_t bytes = (uint32_t)min(max(0, N - kv0), BK) * D * 2;  // one sub-tile: never wraps
+            const i32x4 rk = make_rsrc(K + base + (size_t)min(kv0, N) * D, bytes);
+            const i32x4 rv = make_rsrc(V + base + (size_t)min(kv0, N) * D, bytes);
+#pragma unroll
+            for (int j = 0; j < LPT; ++j) {
+                load_lds_b128(rk, lds_addr(&Ks[g][ST][(j * NT + wave * 64) * 8]), voff[j]);
+                load_lds_b128(rv, lds_addr(&Vs[g][ST][(j * NT + wave * 64) * 8]), voff[j]);
+            }
         }
     };
 
     const __bf16* r_lane[DC];  // K / V rows (A operands of S^T and dP^T)
 #pragma unroll
-    for (int kc = 0; kc < DC; ++kc) r_lane[kc] = &Ks[0][swz<D>(l32, 16 * kc + 8 * half)];
+    for (int kc = 0; kc < DC; ++kc) r_lane[kc] = &Ks[grp][0][swz<D>(l32, 16 * kc + 8 * half)];
     constexpr int V_OFF = (int)(sizeof(Ks) / sizeof(__bf16));  // Vs follows Ks in the same layout
     const int tr_row = 4 * half + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const __bf16* t_lane[2][DB];  // K^T by transposed reads: rows tr_row, tr_row + 8
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        t_lane[0][db] = &Ks[0][swz<D>(tr_row, 32 * db + tr_col)];
-        t_lane[1][db] = &Ks[0][swz<D>(tr_row + 8, 32 * db + tr_col)];
+        t_lane[0][db] = &Ks[grp][0][swz<D>(tr_row, 32 * db + tr_col)];
+        t_lane[1][db] = &Ks[grp][0][swz<D>(tr_row + 8, 32 * db + tr_col)];
     }
 
     // S^T and dP^T of the sub-tile in stage ST: two independent accumulator chains.
@@ -442,9 +496,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         }
     };
     // Causal (key > query) or tail (key >= N) mask of sub-tile t, as -inf scores (P = 0).
-    auto needs_mask = [&](int t) { return CAUSAL ? (t * BK + BK - 1 > wq0) : (t * BK + BK > N); };
-    auto mask = [&](int t, f32x16& s) {
-        const int kv0 = t * BK;
+    auto needs_mask = [&](int i) {
+        const int kv0 = (NG * i + grp) * BK;
+        return CAUSAL ? (kv0 + BK - 1 > wq0) : (kv0 + BK > N);
+    };
+    auto mask = [&](int i, f32x16& s) {
+        const int kv0 = (NG * i + grp) * BK;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 8 * (r / 4) + 4 * half + (r % 4);
@@ -457,7 +514,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], scale_log2, -lse2));
         if constexpr (DROP) {
             uint32_t dm[4];
-            dropout_bytes<true>(drop, (uint32_t)bh, myq, t * BK, lane, dm);
+            dropout_bytes<true>(drop, (uint32_t)bh, myq, (NG * t + grp) * BK, lane, dm);
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] * dropout_factor(dm, r, drop) - del);
         } else {
@@ -517,16 +574,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * 64),
         if (needs_mask(0)) mask(0, sa);
     }
     int i = 0;
-    for (; i + 3 < nt; i += 4) {
+    for (; i + 3 < nsteps; i += 4) {
         step(S0{}, i, sa, da, sbb, dbb);
         step(S1{}, i + 1, sbb, dbb, sa, da);
         step(S2{}, i + 2, sa, da, sbb, dbb);
         step(S3{}, i + 3, sbb, dbb, sa, da);
     }
-    if (i < nt) step(S0{}, i, sa, da, sbb, dbb);
-    if (i + 1 < nt) step(S1{}, i + 1, sbb, dbb, sa, da);
-    if (i + 2 < nt) step(S2{}, i + 2, sa, da, sbb, dbb);
+    if (i < nsteps) step(S0{}, i, sa, da, sbb, dbb);
+    if (i + 1 < nsteps) step(S1{}, i + 1, sbb, dbb, sa, da);
+    if (i + 2 < nsteps) step(S2{}, i + 2, sa, da, sbb, dbb);
     wait_vmcnt<0>();
+
+    if constexpr (NG == 2) {
+        // dQ is a plain sum over keys: group 1's partial joins group 0's through the LDS of
+        // the finished rings, laid out [row block][value][lane].
+        constexpr int NV = DB * 16;
+        static_assert(NW * NV * 64 * 4 <= (int)(sizeof(Ks) + sizeof(Vs)), "merge buffer");
+        float* xs = reinterpret_cast<float*>(&Ks[0][0][0]) + wr * NV * 64 + lane;
+        __syncthreads();  // every wave is done with the rings
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xs[(db * 16 + r) * 64] = dq[db][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[db][r] += xs[(db * 16 + r) * 64];
+    }
 
     if (myq < N) {
         __bf16* row = dQ + base + (size_t)myq * D;
@@ -736,17 +814,39 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
     if ((e = launch_delta<__bf16, D>(a, st)) != hipSuccess) return e;
     if ((e = mark(a, 1, st)) != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL, DROP>), dim3((unsigned)((long long)nkt * a.B * a.H)),
-                       dim3(NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv,
-                       a.N, nkt, a.scale, a.scale * kLog2e, a.drop);
+    const long long ktiles = (long long)nkt * a.B * a.H;
+    bool ksplit = false;  // two query groups per key tile (see dkdv_bf16_kernel)
+    if constexpr (D == 128) {
+        ksplit = ktiles <= kSplitTilesAtMost;
+        if (ksplit)
+            hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL, DROP, 2>), dim3((unsigned)ktiles), dim3(2 * NW * 64),
+                               0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                               (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dk,
+                               (__bf16*)a.dv, a.N, nkt, a.scale, a.scale * kLog2e, a.drop);
+    }
+    if (!ksplit)
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, NW, CAUSAL, DROP, 1>), dim3((unsigned)ktiles),
+                           dim3(NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                           (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dk, (__bf16*)a.dv,
+                           a.N, nkt, a.scale, a.scale * kLog2e, a.drop);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(a, 2, st)) != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL, DROP>), dim3((unsigned)((long long)nqt * a.B * a.H)),
-                       dim3(NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dq, a.N, nqt,
-                       a.scale, a.scale * kLog2e, a.drop);
+    const long long qtiles = (long long)nqt * a.B * a.H;
+    bool split = false;  // two key groups per tile (see dq_bf16_kernel)
+    if constexpr (D == 128) {
+        split = qtiles <= kSplitTilesAtMost;
+        if (split)
+            hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL, DROP, 2>), dim3((unsigned)qtiles),
+                               dim3(2 * NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                               (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dq, a.N,
+                               nqt, a.scale, a.scale * kLog2e, a.drop);
+    }
+    if (!split)
+        hipLaunchKernelGGL((dq_bf16_kernel<D, NW, CAUSAL, DROP, 1>), dim3((unsigned)qtiles),
+                           dim3(NW * 64), 0, st, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                           (const __bf16*)a.dout, (const float*)a.lse2, (const float*)a.delta, (__bf16*)a.dq, a.N, nqt,
+                           a.scale, a.scale * kLog2e, a.drop);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(a, 3, st);
 }

@@ -29,10 +29,6 @@ namespace {
 // reference point (exact in real arithmetic), and most tiles skip the O rescale.
 constexpr float kRescaleSlack = 8.0f;
 
-// Grids of at most this many 128-row tiles (one round of two workgroups per CU) run with two
-// key groups per tile at d = 128.  Measured: 17-25% faster at 64-512 tiles (causal), slower
-// from 640 tiles up, where the grid already fills the machine.
-constexpr long long kSplitTilesAtMost = 512;
 
 // ------------------------------------------------------------------ bf16, MFMA 32x32x16
 // Workgroup: NW waves, each owning QB blocks of 32 query rows (every K/V operand read from

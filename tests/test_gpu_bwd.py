@@ -69,6 +69,24 @@ def test_bwd_head_parts():
     parity_by_head("bwd head parts", [(0, h) for h in range(H)], got, ref, "bf16")
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(1, 2, 8192, True), (1, 1, 5000, False), (2, 3, 1500, True)])
+def test_bwd_groups(B, H, N, causal):
+    """Grids of at most 512 tiles: both backward kernels run two groups of waves per tile,
+    which take alternate sub-tiles and add their partial dQ or dK, dV at the end.  Every
+    element of dQ, dK, dV, including lengths that are not multiples of the tile."""
+    log(f"[bwd] groups B={B} H={H} N={N} causal={causal}")
+    case = fa_inputs.make_case(B, H, N, 128, "bf16", seed=440 + N + H, with_grad=True)
+    dq, dk, dv = run_bwd(case, causal)
+    got = {"dQ": to_f64(dq), "dK": to_f64(dk), "dV": to_f64(dv)}
+    vals = [case[n]["values"] for n in ("q", "k", "v", "do")]
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        r = oracle.backward(*(x[sl] for x in vals), case["scale"], causal)
+        return {"dQ": r[0][0, 0], "dK": r[1][0, 0], "dV": r[2][0, 0]}
+    parity_by_head(f"bwd groups B={B} H={H} N={N}", [(b, h) for b in range(B) for h in range(H)], got, ref, "bf16")
+
+
 def test_bwd_medium_bf16_causal():
     log("[bwd] bf16 causal d=128 N=1000, 2x3 heads")
     case = fa_inputs.make_case(2, 3, 1000, 128, "bf16", seed=301, with_grad=True)
