@@ -29,7 +29,6 @@ namespace {
 // reference point (exact in real arithmetic), and most tiles skip the O rescale.
 constexpr float kRescaleSlack = 8.0f;
 
-
 // ------------------------------------------------------------------ bf16, MFMA 32x32x16
 // Workgroup: NW waves, each owning QB blocks of 32 query rows (every K/V operand read from
 // LDS feeds QB MFMAs).  K/V stream in sub-tiles of 32 keys through an NS-stage
@@ -115,7 +114,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int nt = (kv_end + BK - 1) / BK;
-    // Sub-tiles this wave computes: causal waves stop at their own last row.
     const int nsteps = (nt + NG - 1) / NG;  // steps of the workgroup; step i takes sub-tile NG i + g
     // Steps this wave computes: causal waves stop at their own last row.
     const int wave_last = (wq0 >= N) ? -1 : (CAUSAL ? min(nt, (wq0 + RW - 1) / BK + 1) : nt) - 1;
@@ -131,7 +129,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
     }
     const __bf16* Kh = K + base;
     const __bf16* Vh = V + base;
-    // Enqueue sub-tile t into stage t % NS (= ST).  Tiles at or past N read zeros.
+    // Enqueue step i's sub-tiles (NG i + g for each group g) into stage ST = i % NS of the
+    // groups' rings.  Sub-tiles at or past N read zeros.
     auto issue = [&](auto st, int i) {
         constexpr int ST = decltype(st)::value;
 #pragma unroll
