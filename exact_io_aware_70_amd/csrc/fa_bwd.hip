@@ -116,7 +116,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64), amdgpu_w
     // other query sub-tile of the ring, and the two partial dK, dV add up at the end.
     const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave / NW);
     const int wr = NG == 1 ? wave : wave - grp * NW;
-    const int L = xcd_order(blockIdx.x, gridDim.x, nkt, nkt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nkt);
     int bh, kt;                          // causal: low key tiles see the most queries
     tile_order(L, nkt, gridDim.x / nkt, bh, kt);  // scalar results: this kernel has no VGPR to spare
     const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wr, mykey = kw0 + l32;
@@ -418,7 +418,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
     // sub-tiles 2i + g, and the two partial dQ add up at the end.
     const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave / NW);
     const int wr = NG == 1 ? wave : wave - grp * NW;
-    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int q0 = (nqt - 1 - rank) * BM;  // heaviest (causal) tiles first
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_f32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_order(blockIdx.x, gridDim.x, nkt, nkt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nkt);
     int bh, kt;
     tile_order(L, nkt, gridDim.x / nkt, bh, kt);
     const int k0 = kt * BNK, kw0 = k0 + wave * 32, mykey = kw0 + l32;
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(256, 1) void dq_f32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int q0 = (nqt - 1 - rank) * BM;

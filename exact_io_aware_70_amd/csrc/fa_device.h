@@ -210,14 +210,20 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 //   * Few tiles per head.  With fewer than kPairTilesBelow tiles per head, one head at a time
 //     can leave the last head's heaviest tiles starting after nearly everything else (a
 //     list-scheduling model of 64 slots per XCD loses up to a third at 32 tiles per head and
-//     nothing at 64 or 128).  Heads then go in pairs whose tiles alternate, which removes
-//     the tail; it costs L2 reuse (at N = 8192 it raised the forward's HBM bytes from 1.14x
-//     to 1.52x the compulsory ones), so it is kept to the short case.  An odd head count
-//     leaves the last head on its own.
+//     nothing at 64 or 128).  Heads then go in groups of G (head_group: the smallest power of
+//     two with G x ntiles >= kPairTilesBelow, at most 8) whose tiles are taken rank-major,
+//     the heaviest of all G heads first, which removes the tail.  It costs L2 reuse (pairs at
+//     N = 8192 raised the forward's HBM bytes from 1.14x to 1.52x the compulsory ones), so it
+//     is kept to the short case.  A last, smaller group takes the heads that remain.
 // Both results are uniform and returned through readfirstlane: the integer divisions are
 // expanded on the VALU, and left in VGPRs they turned every address derived from the head
 // into VALU work inside the loops (and cost the 254-VGPR dK/dV kernel a spill).
 constexpr int kPairTilesBelow = 64;
+__device__ __forceinline__ int head_group(int ntiles) {
+    int g = 1;
+    while (g * ntiles < kPairTilesBelow && g < 8) g *= 2;
+    return g;
+}
 __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& head, int& rank) {
     int h, r;
     if (ntiles >= kPairTilesBelow) {
@@ -237,26 +243,25 @@ __device__ __forceinline__ void tile_order(int L, int ntiles, int nheads, int& h
             r = L - h * ntiles;
         }
     } else {
-        const int pair = L / (2 * ntiles), j = L - pair * 2 * ntiles;
-        if (2 * pair + 1 < nheads) {
-            h = 2 * pair + (j & 1);
-            r = j >> 1;
-        } else {
-            h = 2 * pair;
-            r = j;
-        }
+        const int G = head_group(ntiles);
+        const int group = L / (G * ntiles), j = L - group * G * ntiles;
+        const int gs = min(G, nheads - group * G);  // heads in this group (the last may be short)
+        const int i = j / gs;
+        h = group * G + (j - i * gs);
+        r = i;
     }
     head = __builtin_amdgcn_readfirstlane(h);
     rank = __builtin_amdgcn_readfirstlane(r);
 }
 
 // Logical id of workgroup b in a grid of g = nheads x ntiles: the XCD remap, which gives each
-// XCD a contiguous eighth of tile_order's sequence.  Paired heads (fewer than kPairTilesBelow
+// XCD a contiguous eighth of tile_order's sequence.  Head groups (fewer than kPairTilesBelow
 // tiles per head) cannot be cut into equal parts that way, so when an eighth is not a whole
-// number of pairs the ids stay as dispatched, which deals every head's tiles round-robin
+// number of groups the ids stay as dispatched, which deals every head's tiles round-robin
 // over the XCDs.
-__device__ __forceinline__ int xcd_order(int b, int g, int ntiles, bool paired) {
-    return (!paired || g % (16 * ntiles) == 0) ? xcd_remap(b, g) : b;
+__device__ __forceinline__ int xcd_order(int b, int g, int ntiles) {
+    if (ntiles >= kPairTilesBelow) return xcd_remap(b, g);
+    return g % (8 * head_group(ntiles) * ntiles) == 0 ? xcd_remap(b, g) : b;
 }
 
 }  // namespace fa

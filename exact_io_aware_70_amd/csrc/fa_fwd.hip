@@ -91,7 +91,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
     const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave / NW);
     const int wr = NG == 1 ? wave : wave - grp * NW;  // row block of this wave
 
-    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int qt = nqt - 1 - rank;  // heaviest (causal) tiles first
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int q0 = (nqt - 1 - rank) * BM;

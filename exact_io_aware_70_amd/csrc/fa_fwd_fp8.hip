@@ -82,7 +82,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int L = xcd_order(blockIdx.x, gridDim.x, nqt, nqt < kPairTilesBelow);
+    const int L = xcd_order(blockIdx.x, gridDim.x, nqt);
     int bh, rank;
     tile_order(L, nqt, gridDim.x / nqt, bh, rank);
     const int qt = nqt - 1 - rank;  // heaviest (causal) tiles first

@@ -88,6 +88,24 @@ def test_fwd_key_groups(B, H, N, causal, q_scale):
     parity_by_head(f"key groups B={B} H={H} N={N}", [(b, h) for b in range(B) for h in range(H)], got, ref, "bf16")
 
 
+@pytest.mark.parametrize("B,H,N", [(8, 16, 1024), (3, 67, 1000)])
+def test_fwd_head_groups(B, H, N):
+    """Few tiles per head on grids past the key-group split: heads go in groups of up to 8
+    whose tiles are taken heaviest first across the group (201 heads leave a last group of
+    one).  Every element of O and lse, causal."""
+    case = fa_inputs.make_case(B, H, N, 128, "bf16", seed=350 + H)
+    log(f"[fwd] head groups B={B} H={H} N={N}")
+    _, _, _, o, lse = run_fwd(case, True)
+    got = {"O": to_f64(o), "lse": to_f64(lse)}
+    vals = [case[n]["values"] for n in ("q", "k", "v")]
+
+    def ref(b, h):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        r_o, r_lse = oracle.forward(*(x[sl] for x in vals), case["scale"], True)
+        return {"O": r_o[0, 0], "lse": r_lse[0, 0]}
+    parity_by_head(f"head groups B={B} H={H}", [(b, h) for b in range(B) for h in range(H)], got, ref, "bf16")
+
+
 def test_fwd_large_logits_bf16():
     """Q drawn x3 (logits std ~3) with a long causal row: the online rescale is exercised."""
     case = fa_inputs.make_case(1, 4, 2000, 128, "bf16", seed=77, q_scale=3.0)
