@@ -31,9 +31,11 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-m
 # Per-file additions (later flags win): the row softmax promises NaN rows for all -inf
 # input rows, so it keeps IEEE NaN semantics.  The backward kernels are scheduled with the
 # AMDGPU register-pressure trackers: the dK/dV kernel (254 of 256 VGPRs) comes out 1-2%
-# faster, with identical results; the other kernels gain nothing from it.
+# faster, with identical results; the other backward kernels gain nothing from it.  The FP8
+# forward was measured with them too, together with its interleaving strategy.
 FILE_FLAGS = {"fa_softmax.hip": ["-fhonor-nans"],
-              "fa_bwd.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers=1"]}
+              "fa_bwd.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers=1"],
+              "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers=1"]}
 
 
 def hipcc() -> str:

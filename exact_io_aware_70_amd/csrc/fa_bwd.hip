@@ -167,6 +167,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64), amdgpu_w
     // wave writes the (identical) lse / D rows, so each wave issues the same loads.
     auto issue = [&](auto st, int i) {
         constexpr int ST = decltype(st)::value;
+        // One group: nothing is loaded past the end of the walk, so the ring's last NS
+        // sub-tiles are still in their stages when the loop ends (the diagonal pass reads them
+        // there).  Two groups keep loading zeros past the end, which keeps their waits fixed.
+        if (NG == 1 && i >= nsub) return;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const int t = tile_of(i, g);
@@ -278,8 +282,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64), amdgpu_w
     // its body needs no mask; the diagonal sub-tile is done once at the end (below).
     auto step = [&](auto st, int i) {
         constexpr int ST = decltype(st)::value;
-        wait_vmcnt<(NS - 2) * LPS>();  // sub-tile i has landed (this wave's share) ...
-        __syncthreads();               // ... and every wave's; stage (i - 1) % NS is free
+        // Sub-tile i has landed (this wave's share) once at most the loads of the next NS - 2
+        // steps are outstanding; near the end of a one-group walk fewer of those exist.
+        static_assert(NS - 2 == 2, "the waits below assume two steps of loads in flight");
+        if (NG == 2 || i + 2 < nsteps) wait_vmcnt<2 * LPS>();
+        else if (i + 1 < nsteps) wait_vmcnt<LPS>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // ... and every wave's; stage (i - 1) % NS is free
         issue(std::integral_constant<int, (ST + NS - 1) % NS>{}, i + NS - 1);
         const int t = tile_of(i, grp);
         if (!wave_live || (CAUSAL ? t <= wave_first : false)) return;
@@ -306,7 +315,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64), amdgpu_w
     if (i + 2 < nsteps) step(S2{}, i + 2);
     wait_vmcnt<0>();  // the ring's loads have landed ...
 
-    if constexpr (CAUSAL) {
+    if constexpr (CAUSAL && NG == 1) {
+        // Wave w's diagonal sub-tile is ring position nsub - 1 - w, one of the last NS, which
+        // no later load has overwritten: it is read where it is.
+        static_assert(NS >= NW, "the last NW sub-tiles of the walk must all still be in the ring");
+        if (wave_live) {
+            const int st = (nsub - 1 - wr) % NS;
+            body(std::true_type{}, st * STAGE, st, kw0);
+        }
+    }
+    if constexpr (CAUSAL && NG == 2) {
         static_assert(NS >= NW, "each wave needs a stage of its own for its diagonal sub-tile");
         __syncthreads();  // ... and every wave is done reading the ring
         if (grp == 0 && wave_live) {
@@ -551,7 +569,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
         bf16x8 sb[2];
         grad_scores(i, sc, dc, sb);
         chains(std::integral_constant<int, (CUR + 1) % NS>{}, sn, dn);
-        interleave_mfma<2 * DC, 0, 4>();
+        // Without dropout the compiler's own single-wave GEMM interleaving (iglp_opt 1), which
+        // spreads the LDS reads among the S and dP MFMAs, beats the fixed {MFMA, 4 VALU}
+        // groups by 2-3% at d = 128 (equal at d = 64, the same code otherwise); the dropout
+        // form keeps the groups, which serve its mask's VALU work better.
+        if constexpr (DROP) interleave_mfma<2 * DC, 0, 4>();
+        else __builtin_amdgcn_iglp_opt(1);
         asm volatile("" : "+v"(sb[0]), "+v"(sb[1]));  // keep the VALU work in region 1
         dq_product(cur_st, sb);
         if (needs_mask(i + 1)) mask(i + 1, sn);

@@ -256,7 +256,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_
         if (i >= wave_nt) return;
         probs(cur, pb);
         scores(std::integral_constant<int, (CUR + 1) % NS>{}, nxt);
-        interleave_mfma<4, 0, 16>();
+        // The compiler's MFMA / exponential interleaving (iglp_opt 3) places this region's
+        // exponentials, FMAs and conversions among the four S products 2-3% better than fixed
+        // {MFMA, 16 VALU} groups.
+        __builtin_amdgcn_iglp_opt(3);
         asm volatile("" : "+v"(pb));  // keep the exponentials next to the S products
         if (needs_mask(i + 1)) mask(i + 1, nxt);
         pv(cur_st, pb);
