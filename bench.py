@@ -111,20 +111,19 @@ def sources_digest(workload="") -> str:
 def kernel_table(dtype, B, H, N, d, causal):
     """Algorithmic units per launch of each kernel of one step (name -> (bound, units, unit))."""
     cf = 0.5 if causal else 1.0
-    elt = 2 if dtype == "bf16" else 4
     sfx = "bf16" if dtype == "bf16" else "f32"
     n2d = B * H * N * N * d * cf
+    # In launch order: fa_fwd, then fa_bwd's two launches (dQ, then dK/dV).
     return {
         # two products (S = Q K^T, O = P V), 2 N^2 d flops each per head
         f"fwd_{sfx}_kernel": ("mfma", 4.0 * n2d, "flop"),
-        # reads O, dO and lse once; writes D and lse * log2(e), one float each per row
-        "delta_kernel": ("hbm", 2.0 * B * H * N * d * elt + 12.0 * B * H * N, "byte"),
-        # four products: S, dP, dV += P^T dO, dK += dS^T Q
-        f"dkdv_{sfx}_kernel": ("mfma", 8.0 * n2d, "flop"),
         # one product of the method: dQ += dS K.  The kernel also recomputes S and dP, the
         # price of a backward without atomics; those flops are not algorithmic units and are
-        # reported apart (EXECUTED_FACTOR)
+        # reported apart (EXECUTED_FACTOR).  It also forms D = rowsum(dO o O) of its rows (a
+        # reduction with no matrix work, whose extra bytes are O read and D, lse written)
         f"dq_{sfx}_kernel": ("mfma", 2.0 * n2d, "flop"),
+        # four products: S, dP, dV += P^T dO, dK += dS^T Q
+        f"dkdv_{sfx}_kernel": ("mfma", 8.0 * n2d, "flop"),
     }
 
 
@@ -208,7 +207,7 @@ def summarize_pmc(args):
         return copy_bytes / (max(vals) * 1024.0)
 
     ff, fw = calib(fetch), calib(write)
-    names = ["fwd_bf16_kernel", "fwd_f32_kernel", "delta_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
+    names = ["fwd_bf16_kernel", "fwd_f32_kernel", "dkdv_bf16_kernel", "dkdv_f32_kernel",
              "dq_bf16_kernel", "dq_f32_kernel", "softmax_rows_kernel", "fwd_fp8_kernel"] + STD_KERNELS
     out = {}
     for short in names:
@@ -237,7 +236,7 @@ def summarize_pmc(args):
 
 def read_counters(dirs):
     """Mean per dispatch of every counter, per kernel (short name), over rocprofv3 --pmc folders."""
-    names = ["fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"]
+    names = ["fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"]
     per = {}  # (short, counter) -> {dispatch: value}
     for d in dirs:
         for dp, _, files in os.walk(d):
@@ -284,7 +283,7 @@ def summarize_sq(args):
     dur = {}
     with open(stats_csv) as f:
         for r in csv.DictReader(f):
-            for n in ("fwd_bf16_kernel", "delta_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"):
+            for n in ("fwd_bf16_kernel", "dkdv_bf16_kernel", "dq_bf16_kernel", "fwd_fp8_kernel"):
                 if n in r["Name"]:
                     dur[n] = float(r["AverageNs"]) * 1e-9
     c = read_counters(dirs)
@@ -818,7 +817,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ev[0]: before fa_fwd; ev[1..4]: recorded by fa_bwd_timed before its three launches and after.
+    # ev[0]: before fa_fwd; ev[1..]: recorded by fa_bwd_timed before each of its launches and after.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + fa.FA_BWD_LAUNCHES)]
               for _ in range(args.steps)]
     for ev in events:  # create the underlying events before the timed region
@@ -831,7 +830,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # fwd = ev0 -> ev1 (fa_fwd is one launch); then delta, dK/dV, dQ between ev1..ev4.
+    # fwd = ev0 -> ev1 (fa_fwd is one launch); then dQ (with D) and dK/dV between ev1..ev3.
     per = {name: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, name in enumerate(knames)}
     avg = {name: float(np.mean(ts)) for name, ts in per.items()}
     ms_step = wall * 1e3 / args.steps

@@ -22,7 +22,7 @@ __all__ = ["FAError", "library_path", "load_library", "fa_fwd", "fa_bwd", "fa_bw
 FA_OK = 0
 FA_F32 = 0
 FA_BF16 = 1
-FA_BWD_LAUNCHES = 3  # kernel launches per fa_bwd call: D, dK/dV, dQ
+FA_BWD_LAUNCHES = 2  # kernel launches per fa_bwd call: dQ (which also forms D), then dK/dV
 FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # static backward scratch of fa_bwd_noalloc, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -118,14 +118,15 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
                    const float* lse, void* dq, void* dk, void* dv,
                    int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
-/* Number of kernel launches one fa_bwd call makes (D = rowsum(dout * o), dK/dV, dQ). */
-#define FA_BWD_LAUNCHES 3
+/* Number of kernel launches one fa_bwd call makes: dQ, which also forms D = rowsum(dout * o)
+ * and lse * log2(e) into the workspace, then dK/dV. */
+#define FA_BWD_LAUNCHES 2
 
 /*
  * fa_bwd with per-launch timing, for profilers and benchmarks: the same arguments, checks
  * and work as fa_bwd, plus `events`, an array of FA_BWD_LAUNCHES + 1 hipEvent_t handles
  * created (and later destroyed) by the caller.  events[i] is recorded on `stream` right
- * before launch i (0: D, 1: dK/dV, 2: dQ) and events[FA_BWD_LAUNCHES] after the last, so
+ * before launch i (0: dQ with D, 1: dK/dV) and events[FA_BWD_LAUNCHES] after the last, so
  * hipEventElapsedTime(events[i], events[i + 1]) is the duration of launch i.  A NULL array
  * or NULL handle returns FA_ERR_NULL before anything is enqueued; a failed record returns
  * FA_ERR_HIP.  Same passages as fa_bwd ("How FlashAttention Actually Works" -- "The

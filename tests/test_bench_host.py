@@ -23,7 +23,7 @@ def test_refuses_more_than_one_gpu():
 def test_kernel_units_at_the_bench_workload():
     """B=4 H=32 N=8192 d=128 causal: the forward counts 4 B H N^2 d / 2 = 2.199e12 flops
     (the causal forward figure of the survey's shape table); the backward kernels count
-    their own products; the delta kernel moves O and dO (bf16) plus three floats per row."""
+    their own products, listed in launch order (fa_fwd, then fa_bwd's dQ and dK/dV)."""
     t = bench.kernel_table("bf16", 4, 32, 8192, 128, True)
     assert t["fwd_bf16_kernel"][1] == pytest.approx(2.199023e12, rel=1e-6)
     assert t["dkdv_bf16_kernel"][1] == 2 * t["fwd_bf16_kernel"][1]
@@ -33,8 +33,7 @@ def test_kernel_units_at_the_bench_workload():
     assert bench.EXECUTED_FACTOR["dq_bf16_kernel"] * t["dq_bf16_kernel"][1] == 1.5 * t["fwd_bf16_kernel"][1]
     # frac at the measured dQ time of 2.889 ms: 1.0995e12 / 2.889e-3 / 2.5e15 = 0.152
     assert t["dq_bf16_kernel"][1] / 2.889e-3 / 2.5e15 == pytest.approx(0.1522, abs=1e-3)
-    rows = 4 * 32 * 8192
-    assert t["delta_kernel"][1] == 2 * rows * 128 * 2 + 12 * rows
+    assert list(t) == ["fwd_bf16_kernel", "dq_bf16_kernel", "dkdv_bf16_kernel"]
     f = bench.kernel_table("f32", 2, 1, 512, 64, False)
     assert f["fwd_f32_kernel"][1] == 4 * 2 * 512 * 512 * 64
 
@@ -109,5 +108,6 @@ def test_measured_rates_come_from_current_summaries_only(tmp_path, monkeypatch):
     util.write_text(json.dumps({"source_sha256": "0" * 64, "kernels": {}}))
     e = bench.add_measured({"ms": 2.0, "bound": "mfma"}, "dq_bf16_kernel", None, bench.load_util("synthetic"))
     assert e["traffic"] is None and e["hbm_gbs"] is None and e["mfma_busy"] is None
-    h = bench.add_measured({"ms": 1.0, "bound": "hbm"}, "delta_kernel", {"delta_kernel": {"bytes": 8e9}}, None)
+    h = bench.add_measured({"ms": 1.0, "bound": "hbm"}, "softmax_rows_kernel", {"softmax_rows_kernel": {"bytes": 8e9}},
+                           None)
     assert h["hbm_gbs"] == 8000.0 and "mfma_busy" not in h

@@ -123,7 +123,9 @@ def call_bwd_timed(events, **kw):
 
 def test_bwd_timed_rejects_missing_events():
     """fa_bwd_timed needs FA_BWD_LAUNCHES + 1 event handles; NULL array or handle -> FA_ERR_NULL."""
-    assert fa.FA_BWD_LAUNCHES == 3
+    assert fa.FA_BWD_LAUNCHES == 2  # dQ (with D), then dK/dV
+    header = open(os.path.join(os.path.dirname(__file__), "..", "include", "fa.h")).read()
+    assert f"#define FA_BWD_LAUNCHES {fa.FA_BWD_LAUNCHES}\n" in header
     assert call_bwd_timed(None) == -1
     handles = (ctypes.c_void_p * (fa.FA_BWD_LAUNCHES + 1))(*([P] * fa.FA_BWD_LAUNCHES + [None]))
     assert call_bwd_timed(handles) == -1
@@ -208,7 +210,7 @@ def test_dropout_rejects_bad_arguments():
     assert fwd(q=None) == -1
     assert fwd(p=1.0) == -3 and fwd(p=-0.1) == -3 and fwd(p=float("nan")) == -3 and fwd(dtype=0) == -3
     assert bwd(p=1.5) == -3 and bwd(dtype=0) == -3 and bwd(ws=None) == -5
-    events = (ctypes.c_void_p * 4)(P, P, None, P)
+    events = (ctypes.c_void_p * (fa.FA_BWD_LAUNCHES + 1))(P, None, P)
     assert bwd(events=events) == -1
 
 
