@@ -300,7 +300,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
         bf16x8 pb[QB][2];
         probs(cur, pb);
         scores(std::integral_constant<int, (CUR + 1) % NS>{}, nxt);
-        interleave_mfma<DC * QB, 0, 6>();
+        // At d = 64 (half the MFMAs per exponential, four waves per SIMD) the compiler's own
+        // MFMA / exponential interleaving (iglp_opt 2) is 1-2% faster than fixed groups; at
+        // d = 128 every strategy was equal or slower than the {MFMA, 6 VALU} groups.
+        if constexpr (D == 64 && !DROP) __builtin_amdgcn_iglp_opt(2);
+        else interleave_mfma<DC * QB, 0, 6>();
         pin_regs(pb);  // keep the exponentials in region 1 (they would sink to their use)
         if (needs_mask(i + 1)) mask(i + 1, nxt);
         if constexpr (DROP) {
