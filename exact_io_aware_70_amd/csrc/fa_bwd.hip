@@ -43,8 +43,14 @@ namespace {
 // NG = 2 (grids of at most kSplitTilesAtMost key tiles): two groups of NW waves per key tile
 // take alternate query sub-tiles through rings of their own, so the heaviest key tiles' walk
 // halves; group 1's dK, dV partials join group 0's through the LDS at the end.
+// Occupancy: two waves per SIMD at d = 128 (254 of 256 VGPRs); three at d = 64 without
+// dropout, where the kernel fits the 168-VGPR budget without spilling.
+template <int D, bool DROP>
+struct DkdvWaves : std::integral_constant<int, D == 64 && !DROP ? 3 : 2> {};
+
 template <int D, int NW, bool CAUSAL, bool DROP, int NG>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64), amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
+                               amdgpu_waves_per_eu(DkdvWaves<D, DROP>::value, DkdvWaves<D, DROP>::value))) void dkdv_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2,
