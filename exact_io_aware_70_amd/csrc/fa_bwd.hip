@@ -375,10 +375,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, NG * NW * 64),
 // so lse and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T (K^T by transposed
 // reads).  This recomputes S and dP instead of accumulating dQ with atomics.  The prologue
 // also loads the O rows of its queries and forms D = rowsum(dO o O) next to the dO
-// fragments, storing D and lse log2(e) for the dK/dV kernel (the D step of the backward pass,
-// without a launch of its own or a second read of dO).  Software
-// pipeline: the exponentials and dS of sub-tile i run on the VALU while the MFMAs compute
-// S and dP of sub-tile i + 1 (two independent chains), then dQ += K(i)^T dS(i).
+// fragments, storing D and lse log2(e) for the dK/dV kernel (the D step of the backward
+// pass, with no launch of its own and no second read of dO).
+// Software pipeline: the exponentials and dS of sub-tile i run on the VALU while the MFMAs
+// compute S and dP of sub-tile i + 1 (two independent chains), then dQ += K(i)^T dS(i).
 // DROP: dropout (dS = P (Z dP - D) with Z the keep factor).
 // Occupancy: two waves per SIMD at d = 128; three at d = 64, where the kernel fits 168 VGPRs
 // (two with dropout, whose mask would spill at that budget).
@@ -734,7 +734,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ O, const float* __restrict__ LSE,
-    float* __restrict__ Delta, float* __restrict__ dQ, int N, int nqt, float scale, float scale_log2) {
+    float* __restrict__ LSE2, float* __restrict__ Delta, float* __restrict__ dQ, int N, int nqt, float scale,
+    float scale_log2) {
     constexpr int NW = 4, BM = 32 * NW, BN = 32, NT = 256;
     constexpr int ST = D + 1, DB = D / 32;
     __shared__ float Ks[BN * ST], Vs[BN * ST];
@@ -758,7 +759,12 @@ __global__ __launch_bounds__(256, 1) void dq_f32_kernel(
     }
     const float lse_l = (myq < N) ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
     const float del_l = (myq < N) ? sum_halves(acc) : 0.f;
-    if (half == 0 && myq < N) Delta[(size_t)bh * N + myq] = del_l;  // for the dK/dV kernel, which runs next
+    // D for the dK/dV kernel, which runs next; lse log2(e) too, so the workspace holds the same
+    // two arrays on both paths (the fp32 dK/dV kernel forms it from lse itself).
+    if (half == 0 && myq < N) {
+        Delta[(size_t)bh * N + myq] = del_l;
+        LSE2[(size_t)bh * N + myq] = lse_l;
+    }
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
@@ -864,7 +870,8 @@ hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
     const int nqt = (a.N + 127) / 128;
     hipLaunchKernelGGL((dq_f32_kernel<D, CAUSAL>), dim3((unsigned)((long long)nqt * a.B * a.H)), dim3(256), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
-                       (const float*)a.o, a.lse, a.delta, (float*)a.dq, a.N, nqt, a.scale, a.scale * kLog2e);
+                       (const float*)a.o, a.lse, a.lse2, a.delta, (float*)a.dq, a.N, nqt, a.scale,
+                       a.scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(a, 1, st)) != hipSuccess) return e;
     const int nkt = (a.N + 127) / 128;

@@ -38,6 +38,41 @@ def test_bwd_small(dtype, d, causal, N):
         assert_parity(name, to_f64(got), r, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(300, 64), (1000, 128)])
+def test_bwd_workspace_holds_d_and_lse2(dtype, causal, N, d):
+    """The D step of the backward pass, on its own: after fa_bwd the caller's workspace holds
+    D_i = rowsum(dO o O)_i and lse_i log2(e) for every row, in the layout fa.h states (two
+    float [B, H, N] arrays, each rounded up to 256 bytes).  The dQ kernel forms both; dK/dV
+    reads them.  D is compared with the fp64 row sums of the O that fa_fwd stored and of dO,
+    to the fp32 summation bound; lse log2(e) must be the fp32 product exactly.  These small
+    bf16 grids run the one-group dQ kernel at d = 64 and the two-group one at d = 128."""
+    import torch
+    import exact_io_aware_70_amd as fa
+    B, H = 1, 2
+    log(f"[bwd] workspace D, lse2 {dtype} causal={causal} N={N} d={d}")
+    case = fa_inputs.make_case(B, H, N, d, dtype, seed=470 + N, with_grad=True)
+    q, k, v, do = (to_device(case, n) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd(q, k, v, scale=case["scale"], causal=causal)
+    code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d, code), dtype=torch.uint8, device=q.device)
+    fa.fa_bwd(q, k, v, o, lse, do, scale=case["scale"], causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    rows = B * H * N
+    second = -(-rows * 4 // 256) * 256 // 4  # float index where the lse log2(e) array starts
+    wsf = ws.view(torch.float32).cpu().numpy()
+    o64, do64, lse32 = to_f64(o), case["do"]["values"], lse.cpu().numpy().reshape(-1)
+    prod = (o64 * do64).reshape(rows, d)
+    d_ref = prod.sum(axis=1)
+    bound = d * 2.0 ** -23 * np.abs(prod).sum(axis=1) + 1e-30
+    err = np.abs(wsf[:rows].astype(np.float64) - d_ref)
+    log(f"  D: max |err| {err.max():.3e}, max err / bound {(err / bound).max():.3f}")
+    assert np.all(err <= bound)
+    lse2_ref = lse32.astype(np.float32) * np.float32(1.4426950408889634)
+    assert np.array_equal(wsf[second:second + rows], lse2_ref)
+
+
 @pytest.mark.parametrize("B,H", [(1, 3), (1, 5)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_odd_head_counts(B, H, causal):
