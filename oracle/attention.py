@@ -26,7 +26,7 @@ Sources (page title -- section):
   * "How FlashAttention Actually Works" -- "The Secret Weapon: Online Softmax":
     the max is subtracted before exponentiation to avoid overflow.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * causal: key j > query i is masked (square, top-left aligned; diagonal kept);
   * lse is the natural-log logsumexp of the *scaled* logits, lse = m + ln l;
   * gradients for the loss L = sum(O * dO) come from the softmax Jacobian

@@ -7,7 +7,7 @@ imports nothing from it).
 "How FlashAttention Actually Works" -- "The GPU Memory Wall: HBM vs. SRAM" lists dropout
 among the steps of standard attention (matmul, mask, softmax, dropout, matmul) that a fused
 kernel runs on chip.  The pages define neither the random numbers nor where the mask applies;
-this module fixes them (readings listed in the design doc):
+this module fixes them as follows:
 
   * Random numbers: Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
     Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011): a 128-bit counter

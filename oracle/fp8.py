@@ -10,8 +10,8 @@ What it computes is then plain attention of those values, so the oracle decodes 
 exactly (every E4M3 value is a dyadic rational, exact in fp64) and calls the plain
 definition in ``oracle.attention.forward``.  The pages name FP8 support only as a feature
 added by FlashAttention-3 ("How does FlashAttention optimize memory and speed via
-tiling?" -- "Interview tips"); the format and the per-head scaling are readings of this
-build, listed in DESIGN.md.
+tiling?" -- "Interview tips"); the format and the per-head scaling below are readings, not
+the pages' text.
 
 E4M3 (the OCP 8-bit floating-point format, "FN" variant): 1 sign bit, 4 exponent bits
 with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals (m/8) * 2^-6; the

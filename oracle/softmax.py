@@ -19,7 +19,7 @@ Sources (page title -- section):
     computes that pair in one pass and then normalises, which reaches this definition up
     to floating-point summation order.
 
-Readings where the pages are silent (each is listed in the design doc): -inf entries are
+Readings where the pages are silent: -inf entries are
 allowed and give exact zeros; a row whose entries are all -inf has no softmax (0 / 0)
 and yields NaN in every output of the row and in its lse, as the definition evaluates;
 lse is the natural-log logsumexp.  All arithmetic is float64; inputs are upcast exactly.

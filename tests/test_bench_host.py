@@ -21,9 +21,9 @@ def test_refuses_more_than_one_gpu():
 
 
 def test_kernel_units_at_the_bench_workload():
-    """B=4 H=32 N=8192 d=128 causal: the forward counts 4 B H N^2 d / 2 = 2.199e12 flops
-    (the causal forward figure of the survey's shape table); the backward kernels count
-    their own products, listed in launch order (fa_fwd, then fa_bwd's dQ and dK/dV)."""
+    """B=4 H=32 N=8192 d=128 causal: the forward counts 4 B H N^2 d / 2 = 2.199e12 flops;
+    the backward kernels count their own products, listed in launch order (fa_fwd, then
+    fa_bwd's dQ and dK/dV)."""
     t = bench.kernel_table("bf16", 4, 32, 8192, 128, True)
     assert t["fwd_bf16_kernel"][1] == pytest.approx(2.199023e12, rel=1e-6)
     assert t["dkdv_bf16_kernel"][1] == 2 * t["fwd_bf16_kernel"][1]
